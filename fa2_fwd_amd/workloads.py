@@ -1,0 +1,101 @@
+"""Seeded synthetic inputs for the attention forward.
+
+This module only draws random numbers and lays them out; it holds none of the
+attention arithmetic, so both the GPU path's tests and the CPU oracle can take
+their inputs from it.
+
+Recipe: ``torch.Generator('cpu').manual_seed(seed)``, then ``torch.randn`` in
+fp32 for full [B, H, N, d] tensors drawn in the order Q, K, V.  Optionally Q
+and K are multiplied by a power of two after drawing (exact in binary floating
+point), which makes softmax rows peaked.  bf16 workloads round the fp32 draws
+to bf16 with round-to-nearest-even (torch's ``.to(torch.bfloat16)``).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+import math
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str  # "f32" or "bf16"
+    seed: int
+    qk_mult: float = 1.0
+
+    @property
+    def scale(self) -> float:
+        """1/sqrt(d) as the fp32 value both sides use."""
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    @property
+    def flops(self) -> int:
+        """Counted work: the two matrix products, 4*B*H*N^2*d."""
+        return 4 * self.B * self.H * self.N * self.N * self.d
+
+    def describe(self) -> str:
+        extra = f" Q,K x{self.qk_mult:g}" if self.qk_mult != 1.0 else ""
+        return f"attn_fwd B={self.B} H={self.H} N={self.N} d={self.d} {self.dtype}{extra} seed={self.seed}"
+
+
+# The five evaluation shapes: small fp32, the two fp32 sequence lengths of the
+# pages' benchmark table (N=1024, N=2048; the table does not state B, H or d),
+# and two long bf16 sequences.
+CONFIGS = {
+    1: Workload("cfg1", 1, 1, 128, 64, "f32", 1),
+    2: Workload("cfg2", 4, 8, 1024, 64, "f32", 2),
+    3: Workload("cfg3", 4, 8, 2048, 64, "f32", 3, qk_mult=4.0),
+    4: Workload("cfg4", 2, 32, 4096, 128, "bf16", 4),
+    5: Workload("cfg5", 1, 16, 16384, 128, "bf16", 5),
+}
+
+
+def torch_dtype(dtype: str) -> torch.dtype:
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+
+
+def make_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int, qk_mult: float = 1.0):
+    """Host (CPU) tensors q, k, v of shape [B, H, N, d] in ``dtype``, contiguous."""
+    g = torch.Generator("cpu").manual_seed(int(seed))
+    shape = (B, H, N, d)
+    q = torch.randn(shape, generator=g, dtype=torch.float32)
+    k = torch.randn(shape, generator=g, dtype=torch.float32)
+    v = torch.randn(shape, generator=g, dtype=torch.float32)
+    if qk_mult != 1.0:
+        q.mul_(qk_mult)
+        k.mul_(qk_mult)
+    td = torch_dtype(dtype)
+    if td != torch.float32:
+        q, k, v = q.to(td), k.to(td), v.to(td)
+    return q.contiguous(), k.contiguous(), v.contiguous()
+
+
+def workload_inputs(w: Workload):
+    return make_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.qk_mult)
+
+
+def to_oracle_array(t: torch.Tensor) -> np.ndarray:
+    """Host numpy view the oracle accepts: float32, or uint16 bit patterns for bf16."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.float32:
+        return t.numpy()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def sample_rows(N: int, n_random: int, seed: int) -> np.ndarray:
+    """Deterministic query-row sample: tile edges, the middle, the end, plus seeded random rows."""
+    fixed = [0, 1, 63, 64, 127, 128, 255, 256, N // 2, N - 2, N - 1]
+    rng = np.random.default_rng(seed)
+    rnd = rng.integers(0, N, size=n_random) if n_random > 0 else np.empty(0, dtype=np.int64)
+    rows = sorted({int(r) for r in fixed if 0 <= r < N} | {int(r) for r in rnd})
+    return np.asarray(rows, dtype=np.int64)

@@ -1,0 +1,132 @@
+"""CPU oracle for exact attention forward -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product library (``fa2_fwd_amd``)
+never imports, links or calls it, and the two share no code: this side is a
+plain fp64 C++ implementation (``hfa_ref.cpp``) built with g++, driven through
+ctypes.
+
+What it computes (neuralmasteryai "Hardware Acceleration & Custom Kernels",
+section 2, the attention definition; book chapter "Triton and kernel fusion",
+section "Fusion", the stable row softmax):
+
+    s_ij  = scale * sum_c q_ic k_jc          (fp64, whole score row materialised)
+    O_i   = sum_j exp(s_ij - m_i) v_j / sum_j exp(s_ij - m_i),   m_i = max_j s_ij
+    LSE_i = m_i + ln sum_j exp(s_ij - m_i)
+
+``attn_fwd_online`` computes the same quantities by the online normalisation
+identity of that section 2, step 2, tile by tile over the keys.
+
+Inputs are numpy arrays of shape [B, H, N, d]: ``float32`` for fp32 data, or
+``uint16`` holding bf16 bit patterns.  Outputs are fp64.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+LIB_PATH = _HERE / "libhfa_ref.so"
+
+
+def default_threads() -> int:
+    """Host threads the oracle uses: OMP_NUM_THREADS if set, else the CPUs this process may use."""
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        return int(env)
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return max(1, os.cpu_count() or 1)
+
+
+def _prep(q, k, v):
+    arrs = [np.ascontiguousarray(a) for a in (q, k, v)]
+    dt = arrs[0].dtype
+    if any(a.dtype != dt for a in arrs):
+        raise ValueError("q, k, v must share one dtype")
+    if dt == np.float32:
+        code = 0
+    elif dt == np.uint16:
+        code = 1
+    else:
+        raise ValueError("oracle inputs are float32 or uint16 (bf16 bit patterns), got %s" % dt)
+    if arrs[0].ndim != 4 or any(a.shape != arrs[0].shape for a in arrs):
+        raise ValueError("q, k, v must be equal-shape [B, H, N, d] arrays")
+    return arrs, code
+
+
+class OracleLib:
+    """ctypes handle on one build of the oracle library."""
+
+    def __init__(self, path):
+        lib = ctypes.CDLL(str(path))
+        i64 = ctypes.c_int64
+        vp = ctypes.c_void_p
+        lib.hfa_ref_attn_fwd.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i64,
+                                         ctypes.c_double, vp, i64, vp, vp, ctypes.c_int]
+        lib.hfa_ref_attn_fwd.restype = ctypes.c_int
+        lib.hfa_ref_attn_fwd_online.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i64,
+                                                ctypes.c_double, i64, vp, i64, vp, vp, ctypes.c_int]
+        lib.hfa_ref_attn_fwd_online.restype = ctypes.c_int
+        self.lib = lib
+        self.path = str(path)
+
+    def _call(self, fn_name, q, k, v, scale, rows, threads, tile=None):
+        (q, k, v), code = _prep(q, k, v)
+        B, H, N, d = q.shape
+        rows_arr = None
+        if rows is not None:
+            rows_arr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+            R = rows_arr.shape[0]
+        else:
+            R = N
+        o = np.empty((B, H, R, d), dtype=np.float64)
+        lse = np.empty((B, H, R), dtype=np.float64)
+        thr = int(threads) if threads else default_threads()
+        ptr = lambda a: None if a is None else a.ctypes.data  # noqa: E731
+        args = [ptr(q), ptr(k), ptr(v), code, B, H, N, d, float(scale)]
+        if tile is not None:
+            args.append(int(tile))
+        args += [ptr(rows_arr), R if rows_arr is not None else 0, ptr(o), ptr(lse), thr]
+        rc = getattr(self.lib, fn_name)(*args)
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments (%s)" % fn_name)
+        return o, lse
+
+    def attn_fwd(self, q, k, v, scale, rows=None, threads=0):
+        """Definition-form attention forward in fp64.  Returns (O [B,H,R,d], LSE [B,H,R])."""
+        return self._call("hfa_ref_attn_fwd", q, k, v, scale, rows, threads)
+
+    def attn_fwd_online(self, q, k, v, scale, tile, rows=None, threads=0):
+        """Online-normalisation form over key tiles of width ``tile`` (fp64)."""
+        return self._call("hfa_ref_attn_fwd_online", q, k, v, scale, rows, threads, tile=tile)
+
+
+_default = None
+
+
+def default() -> OracleLib:
+    """The oracle built from ``hfa_ref.cpp`` in this directory (built on first use if absent)."""
+    global _default
+    if _default is None:
+        if not LIB_PATH.exists():
+            from oracle.build import build
+
+            build()
+        _default = OracleLib(LIB_PATH)
+    return _default
+
+
+def attn_fwd(q, k, v, scale, rows=None, threads=0):
+    """Definition-form attention forward in fp64.  Returns (O [B,H,R,d], LSE [B,H,R])."""
+    return default().attn_fwd(q, k, v, scale, rows, threads)
+
+
+def attn_fwd_online(q, k, v, scale, tile, rows=None, threads=0):
+    """Online-normalisation form over key tiles of width ``tile`` (fp64)."""
+    return default().attn_fwd_online(q, k, v, scale, tile, rows, threads)

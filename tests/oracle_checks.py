@@ -1,0 +1,304 @@
+"""Checks that pin the CPU oracle against facts fixed outside the oracle itself.
+
+The pages give the definition of attention (neuralmasteryai "Hardware
+Acceleration & Custom Kernels", section 2), the stable row softmax (book
+chapter "Triton and kernel fusion", section "Fusion") and the online
+normalisation identity (same section 2, step 2).  They print no worked numeric
+example (the "Python Simulation" of section 5 is cut off), so the oracle is
+pinned by closed forms, invariants, exact-rational brute force and an
+independent library routine (torch fp64 softmax / logsumexp, the pages' own
+parity baseline being PyTorch eager).
+"""
+
+from fractions import Fraction
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from fa2_fwd_amd import workloads
+
+TIGHT = 1e-12
+
+
+def _rand(shape, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal(shape) * scale).astype(np.float32)
+
+
+def _torch_ref(q, k, v, scale, rows=None):
+    """Independent library routine: torch fp64 softmax(q k^T * scale) v and logsumexp."""
+    q64, k64, v64 = (torch.from_numpy(np.asarray(a, dtype=np.float64)) for a in (q, k, v))
+    if rows is not None:
+        q64 = q64[:, :, torch.as_tensor(rows)]
+    s = torch.matmul(q64, k64.transpose(-1, -2).contiguous()) * scale
+    o = torch.matmul(torch.softmax(s, dim=-1), v64)
+    return o.numpy(), torch.logsumexp(s, dim=-1).numpy()
+
+
+def _widen_bf16(a_u16):
+    return (a_u16.astype(np.uint32) << 16).view(np.float32)
+
+
+# P1 -- softmax rows are stochastic: with V = identity, O is the probability matrix.
+def check_p1_rows_sum_to_one(orc):
+    N = d = 64
+    q = _rand((1, 2, N, d), 1, 4.0)
+    k = _rand((1, 2, N, d), 2, 4.0)
+    v = np.broadcast_to(np.eye(N, d, dtype=np.float32), (1, 2, N, d)).copy()
+    o, _ = orc.attn_fwd(q, k, v, 0.125)
+    assert np.all(o >= 0.0) and np.all(o <= 1.0)
+    np.testing.assert_allclose(o.sum(axis=-1), 1.0, rtol=0, atol=TIGHT)
+
+
+# P2 -- identical keys: every score in a row is equal, so O is the mean of V
+# and LSE = scale * q.k + ln N.
+def check_p2_identical_keys(orc):
+    B, H, N, d = 2, 3, 77, 16
+    q = _rand((B, H, N, d), 3)
+    krow = _rand((B, H, 1, d), 4)
+    k = np.broadcast_to(krow, (B, H, N, d)).copy()
+    v = _rand((B, H, N, d), 5)
+    scale = 0.25
+    o, lse = orc.attn_fwd(q, k, v, scale)
+    np.testing.assert_allclose(o, np.broadcast_to(v.astype(np.float64).mean(axis=2, keepdims=True), o.shape),
+                               rtol=0, atol=TIGHT)
+    qk = np.einsum("bhnd,bhd->bhn", q.astype(np.float64), krow[:, :, 0].astype(np.float64))
+    np.testing.assert_allclose(lse, scale * qk + math.log(N), rtol=0, atol=1e-11)
+
+
+# P3 -- constant V gives that constant for any Q, K, including peaked rows.
+def check_p3_constant_v(orc):
+    B, H, N, d = 1, 2, 129, 64
+    q = _rand((B, H, N, d), 6, 8.0)
+    k = _rand((B, H, N, d), 7, 8.0)
+    c = _rand((1, 1, 1, d), 8)
+    v = np.broadcast_to(c, (B, H, N, d)).copy()
+    o, _ = orc.attn_fwd(q, k, v, 0.125)
+    np.testing.assert_allclose(o, np.broadcast_to(c.astype(np.float64), o.shape), rtol=0, atol=TIGHT)
+
+
+# P4 -- the online identity: any tiling of the keys (tile 1 is the scalar
+# recurrence as stated; tiles >= N/2 are exactly two tiles split at `tile`)
+# equals the one-pass definition.
+def check_p4_online_equals_direct_every_split(orc):
+    B, H, N, d = 1, 2, 40, 8
+    q = _rand((B, H, N, d), 9, 3.0)
+    k = _rand((B, H, N, d), 10, 3.0)
+    v = _rand((B, H, N, d), 11)
+    o_ref, lse_ref = orc.attn_fwd(q, k, v, 0.5)
+    for tile in range(1, N + 1):
+        o, lse = orc.attn_fwd_online(q, k, v, 0.5, tile)
+        np.testing.assert_allclose(o, o_ref, rtol=0, atol=TIGHT, err_msg=f"tile={tile}")
+        np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=TIGHT, err_msg=f"tile={tile}")
+
+
+def check_p4_online_kernel_tiles_peaked(orc):
+    # Peaked rows like the N=2048 workload, with the tile widths the kernels use.
+    B, H, N, d = 1, 1, 300, 64
+    q = _rand((B, H, N, d), 12, 4.0)
+    k = _rand((B, H, N, d), 13, 4.0)
+    v = _rand((B, H, N, d), 14)
+    o_ref, lse_ref = orc.attn_fwd(q, k, v, 0.125)
+    for tile in (16, 32, 64, 128):
+        o, lse = orc.attn_fwd_online(q, k, v, 0.125, tile)
+        np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-11)
+        np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-11)
+
+
+# P5 -- brute force on tiny inputs.
+def check_p5_single_key(orc):
+    q = _rand((1, 1, 1, 8), 15)
+    k = _rand((1, 1, 1, 8), 16)
+    v = _rand((1, 1, 1, 8), 17)
+    o, lse = orc.attn_fwd(q, k, v, 0.3)
+    np.testing.assert_array_equal(o[0, 0, 0], v[0, 0, 0].astype(np.float64))
+    s = 0.3 * float(np.dot(q[0, 0, 0].astype(np.float64), k[0, 0, 0].astype(np.float64)))
+    assert abs(lse[0, 0, 0] - s) < TIGHT
+
+
+def check_p5_two_keys_logistic(orc):
+    q = _rand((1, 1, 2, 4), 18)
+    k = _rand((1, 1, 2, 4), 19)
+    v = _rand((1, 1, 2, 4), 20)
+    scale = 0.7
+    o, lse = orc.attn_fwd(q, k, v, scale)
+    q64, k64, v64 = (a[0, 0].astype(np.float64) for a in (q, k, v))
+    for i in range(2):
+        s0, s1 = scale * q64[i] @ k64[0], scale * q64[i] @ k64[1]
+        p0 = 1.0 / (1.0 + math.exp(s1 - s0))  # logistic closed form
+        np.testing.assert_allclose(o[0, 0, i], p0 * v64[0] + (1 - p0) * v64[1], rtol=0, atol=TIGHT)
+        assert abs(lse[0, 0, i] - np.logaddexp(s0, s1)) < TIGHT
+
+
+def check_p5_exact_rational(orc):
+    # d = 1, q = 1, integer keys, scale = ln 2: p_j is proportional to 2^k_j,
+    # so O = sum 2^k_j v_j / sum 2^k_j is an exact rational for dyadic v.
+    keys = [-7, 3, 0, 12, 12, -20, 5, 1, 9]
+    vals = [Fraction(n, 8) for n in (3, -5, 11, 1, -2, 7, 0, 13, -9)]
+    N = len(keys)
+    q = np.ones((1, 1, N, 1), np.float32)
+    k = np.asarray(keys, np.float32).reshape(1, 1, N, 1)
+    v = np.asarray([float(x) for x in vals], np.float32).reshape(1, 1, N, 1)
+    o, lse = orc.attn_fwd(q, k, v, math.log(2.0))
+    den = sum(Fraction(2) ** kj for kj in keys)
+    num = sum(Fraction(2) ** kj * vj for kj, vj in zip(keys, vals))
+    exact_o = float(num / den)
+    exact_lse = math.log(2.0) * math.log2(float(den))
+    np.testing.assert_allclose(o[0, 0, :, 0], exact_o, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse[0, 0], exact_lse, rtol=0, atol=1e-12)
+
+
+# P6 -- scale 0: uniform weights, O = mean V, LSE = ln N.
+def check_p6_zero_scale(orc):
+    B, H, N, d = 1, 2, 50, 16
+    q, k, v = _rand((B, H, N, d), 21), _rand((B, H, N, d), 22), _rand((B, H, N, d), 23)
+    o, lse = orc.attn_fwd(q, k, v, 0.0)
+    np.testing.assert_allclose(o, np.broadcast_to(v.astype(np.float64).mean(axis=2, keepdims=True), o.shape),
+                               rtol=0, atol=TIGHT)
+    np.testing.assert_allclose(lse, math.log(N), rtol=0, atol=TIGHT)
+
+
+# P7 -- adding one vector c to every key shifts every score of row i by
+# scale * q_i.c: O is unchanged and LSE moves by exactly that amount.
+def check_p7_key_shift(orc):
+    rng = np.random.default_rng(24)
+    B, H, N, d = 1, 1, 64, 16
+    q = rng.integers(-3, 4, (B, H, N, d)).astype(np.float32)
+    k = rng.integers(-3, 4, (B, H, N, d)).astype(np.float32)
+    v = _rand((B, H, N, d), 25)
+    c = rng.integers(-5, 6, (1, 1, 1, d)).astype(np.float32)
+    scale = 0.25
+    o0, lse0 = orc.attn_fwd(q, k, v, scale)
+    o1, lse1 = orc.attn_fwd(q, k + c, v, scale)
+    np.testing.assert_allclose(o1, o0, rtol=0, atol=TIGHT)
+    shift = scale * np.einsum("bhnd,d->bhn", q.astype(np.float64), c[0, 0, 0].astype(np.float64))
+    np.testing.assert_allclose(lse1, lse0 + shift, rtol=0, atol=1e-11)
+
+
+# P8 -- a joint permutation of the keys and values changes nothing; a
+# permutation of the queries permutes the output rows.
+def check_p8_permutations(orc):
+    B, H, N, d = 1, 2, 70, 16
+    q, k, v = _rand((B, H, N, d), 26, 2.0), _rand((B, H, N, d), 27, 2.0), _rand((B, H, N, d), 28)
+    o, lse = orc.attn_fwd(q, k, v, 0.25)
+    perm = np.random.default_rng(29).permutation(N)
+    o_kv, lse_kv = orc.attn_fwd(q, k[:, :, perm], v[:, :, perm], 0.25)
+    np.testing.assert_allclose(o_kv, o, rtol=0, atol=TIGHT)
+    np.testing.assert_allclose(lse_kv, lse, rtol=0, atol=TIGHT)
+    o_q, lse_q = orc.attn_fwd(q[:, :, perm], k, v, 0.25)
+    np.testing.assert_allclose(o_q, o[:, :, perm], rtol=0, atol=TIGHT)
+    np.testing.assert_allclose(lse_q, lse[:, :, perm], rtol=0, atol=TIGHT)
+
+
+# P9 -- cross-check against torch's fp64 softmax / logsumexp on the five
+# evaluation shapes (whole for the two small ones, sampled rows otherwise).
+def check_p9_library_crosscheck(orc, cfg):
+    w = workloads.CONFIGS[cfg]
+    q, k, v = workloads.workload_inputs(w)
+    qa, ka, va = (workloads.to_oracle_array(t) for t in (q, k, v))
+    rows = None if cfg <= 2 else workloads.sample_rows(w.N, 8, seed=100 + cfg)
+    o, lse = orc.attn_fwd(qa, ka, va, w.scale, rows=rows)
+    if w.dtype == "bf16":
+        qa, ka, va = (_widen_bf16(a) for a in (qa, ka, va))
+    o_t, lse_t = _torch_ref(qa, ka, va, w.scale, rows)
+    np.testing.assert_allclose(o, o_t, rtol=0, atol=1e-11)
+    np.testing.assert_allclose(lse, lse_t, rtol=0, atol=1e-11)
+
+
+# P10 -- one key leading every other score by > 40: O is that key's value row
+# to within e^-40 relative weight.
+def check_p10_peaked_limit(orc):
+    B, H, N, d = 1, 1, 33, 16
+    rng = np.random.default_rng(30)
+    q = np.zeros((B, H, N, d), np.float32)
+    q[..., 0] = 20.0
+    k = (rng.standard_normal((B, H, N, d)) * 0.1).astype(np.float32)
+    k[0, 0, 17, 0] = 20.0
+    v = _rand((B, H, N, d), 31)
+    o, lse = orc.attn_fwd(q, k, v, 0.25)
+    bound = N * math.exp(-40.0) * float(np.abs(v).max())
+    np.testing.assert_allclose(o[0, 0], np.broadcast_to(v[0, 0, 17].astype(np.float64), (N, d)),
+                               rtol=0, atol=bound)
+
+
+def check_rejects_bad_arguments(orc):
+    q = _rand((1, 1, 4, 4), 32)
+    with pytest.raises(ValueError):
+        orc.attn_fwd(q, q, q, float("nan"))
+    with pytest.raises(ValueError):
+        orc.attn_fwd(q, q, q, 1.0, rows=[0, 4])
+    with pytest.raises(ValueError):
+        orc.attn_fwd_online(q, q, q, 1.0, 0)
+    with pytest.raises(ValueError):
+        orc.attn_fwd(q.astype(np.float64), q, q, 1.0)
+
+
+def check_bf16_widening_is_exact(orc):
+    # bf16 inputs reach the oracle as bit patterns; check the widened values
+    # against torch's own bf16 -> fp64 conversion.
+    q, k, v = workloads.make_inputs(1, 1, 64, 16, "bf16", 33)
+    qa, ka, va = (workloads.to_oracle_array(t) for t in (q, k, v))
+    o, lse = orc.attn_fwd(qa, ka, va, 0.25)
+    o_t, lse_t = _torch_ref(q.double().numpy(), k.double().numpy(), v.double().numpy(), 0.25)
+    np.testing.assert_allclose(o, o_t, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(lse, lse_t, rtol=0, atol=1e-13)
+
+
+def check_p9_small_sampled(orc):
+    # Same library cross-check on a small bf16 problem with a row sample, so
+    # that the row-selection bookkeeping is exercised quickly.
+    q, k, v = workloads.make_inputs(1, 2, 200, 32, "bf16", 34)
+    qa, ka, va = (workloads.to_oracle_array(t) for t in (q, k, v))
+    rows = np.asarray([0, 5, 63, 64, 150, 199], np.int64)
+    o, lse = orc.attn_fwd(qa, ka, va, 0.2, rows=rows)
+    o_t, lse_t = _torch_ref(q.double().numpy(), k.double().numpy(), v.double().numpy(), 0.2, rows)
+    np.testing.assert_allclose(o, o_t, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_t, rtol=0, atol=1e-12)
+
+
+ALL_CHECKS = [
+    check_p1_rows_sum_to_one,
+    check_p2_identical_keys,
+    check_p3_constant_v,
+    check_p4_online_equals_direct_every_split,
+    check_p4_online_kernel_tiles_peaked,
+    check_p5_single_key,
+    check_p5_two_keys_logistic,
+    check_p5_exact_rational,
+    check_p6_zero_scale,
+    check_p7_key_shift,
+    check_p8_permutations,
+    check_p10_peaked_limit,
+    check_rejects_bad_arguments,
+    check_bf16_widening_is_exact,
+    check_p9_small_sampled,
+    lambda orc: check_p9_library_crosscheck(orc, 1),
+]
+
+
+def check_golden_exact_rational(orc):
+    # Stored hand derivation (tests/golden/exact_rational.txt).
+    import os
+
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "exact_rational.txt")
+    fields = {}
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            key, *vals = line.split()
+            fields[key] = [float(x) for x in vals]
+    keys, vals = fields["keys"], fields["values"]
+    N = len(keys)
+    q = np.ones((1, 1, N, 1), np.float32)
+    k = np.asarray(keys, np.float32).reshape(1, 1, N, 1)
+    v = np.asarray(vals, np.float32).reshape(1, 1, N, 1)
+    o, lse = orc.attn_fwd(q, k, v, math.log(2.0))
+    exact_o = fields["o_num"][0] / fields["o_den"][0]
+    exact_lse = math.log(fields["lse_arg_num"][0] / fields["lse_arg_den"][0])
+    np.testing.assert_allclose(o[0, 0, :, 0], exact_o, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], exact_lse, rtol=0, atol=1e-14)
+
+
+ALL_CHECKS.append(check_golden_exact_rational)

@@ -1,0 +1,48 @@
+"""Planted mistakes in the oracle, on the CPU: every plausible slip must fail a pin.
+
+Each case copies ``oracle/hfa_ref.cpp``, applies one textual mistake (a dropped
+term, a wrong sign, a wrong index, a missing rescale), builds the copy into a
+temporary library and runs the pins against it.  The case passes when at least
+one pin rejects the mutated oracle.  Nothing here touches a GPU.
+"""
+
+import pytest
+
+import oracle
+from oracle.build import SOURCE, build
+import oracle_checks as C
+
+MUTATIONS = {
+    "no_max_subtraction": ("S[j] = std::exp(S[j] - m);", "S[j] = std::exp(S[j]);"),
+    "wrong_sign_exponent": ("S[j] = std::exp(S[j] - m);", "S[j] = std::exp(m - S[j]);"),
+    "dropped_scale": ("S[j] = scale * dot;", "S[j] = dot;"),
+    "no_normalisation": ("out[c] = num / l;", "out[c] = num;"),
+    "lse_without_max": ("*lse_out = m + std::log(l);", "*lse_out = std::log(l);"),
+    "value_column_index": ("num += S[j] * V[j * d + c];", "num += S[j] * V[j * d + (d - 1 - c)];"),
+    "key_column_index": ("dot += qrow[c] * K[j * d + c];", "dot += qrow[c] * K[j * d + (d - 1 - c)];"),
+    "dropped_first_term": ("    l += S[j];", "    if (j > 0) l += S[j];"),
+    "online_no_denominator_rescale": ("l = l * alpha + tile_sum;", "l = l + tile_sum;"),
+    "online_no_accumulator_rescale": ("for (int64_t c = 0; c < d; ++c) acc[c] *= alpha;", ""),
+    "online_alpha_sign": ("std::exp(m_old - m_new);", "std::exp(m_new - m_old);"),
+    "bf16_widen_shift": ("<< 16;", "<< 15;"),
+    "sampled_row_index": ("(h * P.N + i) * P.d + c", "(h * P.N + r) * P.d + c"),
+    "keys_as_queries": ("qrow[c] = widen(P.q,", "qrow[c] = widen(P.k,"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_reject_planted_mistake(name, tmp_path):
+    before, after = MUTATIONS[name]
+    text = SOURCE.read_text()
+    assert text.count(before) == 1, f"mutation anchor for {name} not unique in the oracle source"
+    src = tmp_path / "hfa_ref_mut.cpp"
+    src.write_text(text.replace(before, after))
+    lib = build(src=src, out=tmp_path / "libhfa_ref_mut.so")
+    orc = oracle.OracleLib(lib)
+    failed = []
+    for check in C.ALL_CHECKS:
+        try:
+            check(orc)
+        except (AssertionError, ValueError, FloatingPointError):
+            failed.append(getattr(check, "__name__", "check"))
+    assert failed, f"no pin rejects the planted mistake {name}"
