@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Attention-forward benchmark on one MI355X: TFLOP/s and fraction of the MFMA roofline.
+
+A step is one attention forward (the whole fused kernel) over one batch of
+synthetic inputs already resident in HBM.  Default workload: B=1, H=16,
+N=16384, d=128, bf16 (the long-sequence headline shape); the N=2048 fp32
+shape (B=4, H=8, d=64, Q and K x4) is timed beside it as "secondary".
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+
+Modes:
+  python bench.py [--steps K] [--warmup W] [--config 5] [--secondary 3]
+  python bench.py --profile-pass --config C     (a few launches plus a plain
+      device copy of known size, for rocprofv3 counter runs)
+  python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --config C
+      (turns two rocprofv3 --pmc outputs into profiles/traffic.json)
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published dense matrix-core peaks (TFLOP/s) and HBM bandwidth (GB/s).
+MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "f64": 78.6}
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_BYTES = 512 * 1024 * 1024  # calibration copy for the HBM byte counters
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest() -> str:
+    """Digest of the HIP sources: counter figures are only valid for the kernel they were taken on."""
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "fa2_fwd_amd", "csrc", "*"))):
+        with open(path, "rb") as f:
+            h.update(os.path.basename(path).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_key(w) -> str:
+    return f"attn_fwd_{w.dtype}_d{w.d}"
+
+
+def algorithmic_bytes(w) -> int:
+    """Q, K, V read once and O written once (elt bytes each) plus LSE (fp32)."""
+    elt = 4 if w.dtype == "f32" else 2
+    return 4 * w.B * w.H * w.N * w.d * elt + 4 * w.B * w.H * w.N
+
+
+def load_traffic(w):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = table.get(kernel_key(w) + f"_N{w.N}")
+    if not entry or entry.get("src_digest") != kernel_source_digest():
+        return None
+    return entry
+
+
+def time_gpu(w, steps: int, warmup: int):
+    import torch
+
+    import fa2_fwd_amd as hfa
+    from fa2_fwd_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    log(f"[bench] {w.describe()}: generating inputs")
+    q, k, v = (t.to(dev) for t in W.workload_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(warmup):
+        hfa.attn_fwd(q, k, v, w.scale, out=o, lse=lse, stream=stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        hfa.attn_fwd(q, k, v, w.scale, out=o, lse=lse, stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / steps
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    peak = MFMA_PEAK_TFLOPS[w.dtype]
+    log(f"[bench] {w.describe()}: {ms:.4f} ms/launch, {tflops:.1f} TFLOP/s, {100 * tflops / peak:.1f}% of "
+        f"{w.dtype} MFMA peak (wall {wall:.3f} s for {steps} steps)")
+    traffic = load_traffic(w)
+    roofline = {
+        "bound": "mfma",
+        "achieved": round(tflops, 3),
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": round(tflops / peak, 4),
+        "traffic": None if traffic is None else int(traffic["hbm_bytes_per_launch"]),
+        "algorithmic_bytes": algorithmic_bytes(w),
+        "kernel": kernel_key(w),
+    }
+    return {"ms": ms, "tflops": tflops, "wall_s": wall, "roofline": roofline}
+
+
+def cpu_baseline(w, target_s: float):
+    """The fp64 oracle, as it is, on a bounded sample of query rows of the same workload."""
+    import numpy as np
+
+    import oracle
+    from fa2_fwd_amd import workloads as W
+
+    qa, ka, va = (W.to_oracle_array(t) for t in W.workload_inputs(w))
+    threads = oracle.default_threads()
+    heads = w.B * w.H
+
+    def run(rows_per_head):
+        rows = np.linspace(0, w.N - 1, rows_per_head).round().astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.attn_fwd(qa, ka, va, w.scale, rows=rows, threads=threads)
+        return time.perf_counter() - t0
+
+    # Two short calibration runs separate the per-head widening cost from the
+    # per-row cost; the measured run is then sized to about target_s.
+    r0, r1 = min(w.N, 8), min(w.N, 40)
+    t0, t1 = run(r0), run(r1)
+    per_row = max((t1 - t0) / max(r1 - r0, 1), 1e-6)
+    fixed = max(t0 - per_row * r0, 0.0)
+    r = int(min(w.N, max(r1, round((target_s - fixed) / per_row))))
+    t = run(r)
+    flops = 4 * heads * r * w.N * w.d
+    value = flops / t / 1e12
+    log(f"[bench] oracle: {r} rows/head x {heads} heads in {t:.2f} s on {threads} threads "
+        f"-> {value * 1e3:.2f} GFLOP/s")
+    return {
+        "value": value,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{r} of {w.N} query rows per head (evenly spaced) x {heads} heads, full key length, "
+                  f"fp64 definition with the score rows materialised; {t:.2f} s",
+    }
+
+
+def profile_pass(w, launches: int) -> None:
+    """A few kernel launches and one device copy of COPY_BYTES, for counter runs."""
+    import torch
+
+    import fa2_fwd_amd as hfa
+    from fa2_fwd_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in W.workload_inputs(w))
+    for _ in range(launches):
+        hfa.attn_fwd(q, k, v, w.scale)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[profile] {launches} launches of {w.describe()} and one {COPY_BYTES} B copy done")
+
+
+def _read_counter(dirpath: str, counter: str):
+    """Per-dispatch (kernel name, value) from a rocprofv3 counter_collection.csv."""
+    files = glob.glob(os.path.join(dirpath, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no counter_collection.csv under {dirpath}")
+    out = []
+    for path in files:
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") == counter:
+                    out.append((row.get("Kernel_Name", ""), float(row["Counter_Value"])))
+    return out
+
+
+def summarize_pmc(w, fetch_dir: str, write_dir: str) -> None:
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel, each scaled
+    by what the same counter reads for the copy of known size."""
+    result = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _read_counter(d, counter)
+        attn = [v for name, v in rows if "attn_fwd" in name]
+        # The device-to-device copy is HIP's blit kernel; fall back to the
+        # largest non-attention dispatch if the runtime names it differently.
+        copies = [v for name, v in rows if "copyBuffer" in name]
+        if not copies:
+            copies = [v for name, v in rows if "attn_fwd" not in name and v * 1024 > COPY_BYTES * 0.25]
+        if not attn or not copies:
+            raise RuntimeError(f"{counter}: missing attention ({len(attn)}) or copy ({len(copies)}) dispatches")
+        copy_kib = max(copies)
+        factor = (COPY_BYTES / 1024) / copy_kib
+        attn_kib = sum(attn) / len(attn)
+        result[counter] = {"attn_kib_per_dispatch": attn_kib, "copy_kib": copy_kib, "scale": factor,
+                           "bytes_per_launch": attn_kib * 1024 * factor}
+    table = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    total = result["FETCH_SIZE"]["bytes_per_launch"] + result["WRITE_SIZE"]["bytes_per_launch"]
+    table[kernel_key(w) + f"_N{w.N}"] = {
+        "workload": w.describe(),
+        "src_digest": kernel_source_digest(),
+        "fetch": result["FETCH_SIZE"],
+        "write": result["WRITE_SIZE"],
+        "hbm_bytes_per_launch": total,
+        "algorithmic_bytes": algorithmic_bytes(w),
+    }
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(table, f, indent=2, sort_keys=True)
+        f.write("\n")
+    log(f"[pmc] {w.describe()}: HBM {total / 1e6:.1f} MB/launch vs algorithmic {algorithmic_bytes(w) / 1e6:.1f} MB")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=5, help="workload number 1-5 (default 5)")
+    ap.add_argument("--secondary", type=int, default=3, help="second workload timed beside it (0: none)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-pass", action="store_true")
+    ap.add_argument("--launches", type=int, default=3)
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    args = ap.parse_args()
+
+    from fa2_fwd_amd import workloads as W
+
+    w = W.CONFIGS[args.config]
+    if args.summarize_pmc:
+        summarize_pmc(w, *args.summarize_pmc)
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this attention forward is a single-GPU kernel; "
+              "see the design notes for how it would shard across GPUs.", file=sys.stderr)
+        return 2
+    if args.profile_pass:
+        profile_pass(w, args.launches)
+        return 0
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    main_res = time_gpu(w, args.steps, args.warmup)
+    secondary = None
+    if args.secondary and args.secondary != args.config:
+        w2 = W.CONFIGS[args.secondary]
+        r2 = time_gpu(w2, args.steps, args.warmup)
+        secondary = {
+            "metric": "attention fwd TFLOP/s",
+            "value": round(r2["tflops"], 3),
+            "unit": "TFLOP/s",
+            "ms_per_step": round(r2["ms"], 5),
+            "dtype": w2.dtype,
+            "config": {"workload": w2.describe(), "B": w2.B, "H": w2.H, "N": w2.N, "d": w2.d},
+            "roofline": r2["roofline"],
+        }
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
+    props = torch.cuda.get_device_properties(0)
+    line = {
+        "metric": "attention fwd TFLOP/s (4*B*H*N^2*d per launch) and fraction of MFMA peak",
+        "value": round(main_res["tflops"], 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1))",
+        "config": {"workload": w.describe(), "B": w.B, "H": w.H, "N": w.N, "d": w.d, "seed": w.seed},
+        "roofline": main_res["roofline"],
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+        "device": getattr(props, "gcnArchName", props.name),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,1 +1,136 @@
-"""MI355X-native exact attention forward (FlashAttention-2 style)."""
+"""MI355X-native exact attention forward (FlashAttention-2 style online softmax).
+
+A thin ctypes binding over ``libhfa.so`` (C ABI in ``include/hfa.h``).  The
+functions named like the C entry points pass raw pointers straight through;
+``attn_fwd`` does the argument marshalling for torch tensors on a gfx950
+device (torch supplies device memory and the current stream, nothing else).
+Every step of the computation runs in the library's HIP kernels: there is no
+fallback path, and a missing or unloadable library raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from pathlib import Path
+
+_PKG = Path(__file__).resolve().parent
+LIB_PATH = _PKG / "libhfa.so"
+
+HFA_F32 = 0
+HFA_BF16 = 1
+
+HFA_OK = 0
+HFA_ERR_NULL = 1
+HFA_ERR_SHAPE = 2
+HFA_ERR_UNSUPPORTED = 3
+HFA_ERR_SCALE = 4
+HFA_ERR_ALIGN = 5
+HFA_ERR_ALIAS = 6
+HFA_ERR_NO_DEVICE = 7
+HFA_ERR_LAUNCH = 8
+
+EXPORTED = ("hfa_attn_fwd", "hfa_status_str", "hfa_block_rows")
+
+_lib = None
+
+
+class HfaError(RuntimeError):
+    """A status other than HFA_OK returned by the library."""
+
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"hfa status {status}: {hfa_status_str(status)}")
+
+
+def load_library(path: str | Path | None = None) -> ctypes.CDLL:
+    """Load ``libhfa.so`` (building it first if it has never been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = Path(path) if path is not None else LIB_PATH
+    if not p.exists():
+        if path is not None:
+            raise FileNotFoundError(p)
+        from fa2_fwd_amd.build import build
+
+        build()
+    lib = ctypes.CDLL(str(p))
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.hfa_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int, vp]
+    lib.hfa_attn_fwd.restype = ctypes.c_int
+    lib.hfa_status_str.argtypes = [ctypes.c_int]
+    lib.hfa_status_str.restype = ctypes.c_char_p
+    lib.hfa_block_rows.argtypes = [ctypes.c_int, i64]
+    lib.hfa_block_rows.restype = i64
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def hfa_attn_fwd(q, k, v, o, lse, B, H, N, d, scale, dtype, stream) -> int:
+    """Raw C-ABI call: every pointer an int (device address) or None; returns the status."""
+    return load_library().hfa_attn_fwd(q, k, v, o, lse, B, H, N, d, scale, dtype, stream)
+
+
+def hfa_status_str(status: int) -> str:
+    return load_library().hfa_status_str(int(status)).decode()
+
+
+def hfa_block_rows(dtype: int, d: int) -> int:
+    return int(load_library().hfa_block_rows(int(dtype), int(d)))
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return HFA_F32
+    if t.dtype == torch.bfloat16:
+        return HFA_BF16
+    raise ValueError(f"attn_fwd supports float32 and bfloat16, got {t.dtype}")
+
+
+def attn_fwd(q, k, v, scale: float | None = None, out=None, lse=None, stream=None):
+    """O, LSE = attention forward of device tensors q, k, v of shape [B, H, N, d].
+
+    ``scale`` defaults to 1/sqrt(d).  ``out`` ([B,H,N,d], q's dtype) and ``lse``
+    ([B,H,N] float32) may be given to write into caller buffers.  The kernel is
+    enqueued on ``stream`` (default: torch's current stream) and not waited for.
+    Raises ValueError on dtype, shape, device or contiguity mismatch and
+    HfaError on a library error.
+    """
+    import torch
+
+    tensors = (q, k, v)
+    if any(not isinstance(t, torch.Tensor) for t in tensors):
+        raise ValueError("q, k, v must be torch tensors")
+    if q.ndim != 4 or k.shape != q.shape or v.shape != q.shape:
+        raise ValueError("attn_fwd needs equal-shape [B, H, N, d] tensors")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share one dtype")
+    code = _dtype_code(q)
+    if any(not t.is_cuda for t in tensors) or k.device != q.device or v.device != q.device:
+        raise ValueError("q, k, v must be on the same GPU device")
+    if any(not t.is_contiguous() for t in tensors):
+        raise ValueError("attn_fwd needs contiguous tensors")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype or out.device != q.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like q")
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, H, N) or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    with torch.cuda.device(q.device):
+        st = hfa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                          B, H, N, d, float(scale), code, handle)
+    if st != HFA_OK:
+        raise HfaError(st)
+    return out, lse

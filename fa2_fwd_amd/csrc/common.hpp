@@ -1,0 +1,64 @@
+// Shared device helpers for the gfx950 attention kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hfa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr double kLn2 = 0.69314718055994530942;
+
+// Workgroups are handed out round-robin over the 8 XCDs (wg % 8 selects the
+// XCD).  Remap the hardware id so that each XCD receives one contiguous range
+// of logical tiles: tiles of one (batch, head) then share that XCD's L2 for
+// their common K/V stream.  A bijection on [0, total).
+__device__ __forceinline__ int xcd_remap(int wg, int total) {
+  constexpr int kXcd = 8;
+  const int per = total / kXcd, rem = total % kXcd;
+  const int xcd = wg % kXcd, local = wg / kXcd;
+  return (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+// 2^x on the hardware exp unit (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Exchange with the lane 32 apart (v_permlane32_swap): returns {own, partner}
+// in an order that depends on the half, so use it only in symmetric ops.
+__device__ __forceinline__ float max_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ void lds_store16(char* lds, int byte_off, u32x4 v) {
+  *reinterpret_cast<u32x4*>(lds + byte_off) = v;
+}
+__device__ __forceinline__ u32x4 lds_load16(const char* lds, int byte_off) {
+  return *reinterpret_cast<const u32x4*>(lds + byte_off);
+}
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane j supplies the address of 4 consecutive 16-bit elements; lane i
+// receives element (i % 4) of the vectors read by lanes i/4, 4 + i/4, 8 + i/4
+// and 12 + i/4.  With lane j pointing at row j/4, columns 4*(j%4)..+3 of a
+// 4 x 16 block, lane i therefore gets column i of the 4 rows.
+__device__ __forceinline__ s16x4 lds_read_tr16(const char* lds, int byte_off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(const_cast<char*>(lds) + byte_off));
+}
+
+}  // namespace hfa

@@ -1,0 +1,179 @@
+// C ABI of libhfa.so (declared in include/hfa.h): argument validation, device
+// check and kernel dispatch for the gfx950 attention forward.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/hfa.h"
+#include "attn_bf16.hpp"
+#include "attn_f32.hpp"
+
+namespace {
+
+using namespace hfa;
+
+// Tile configurations, one per (dtype, head dim).
+using Bf16D128 = Bf16Tile<128, 1, 4>;
+using Bf16D64 = Bf16Tile<64, 1, 4>;
+using F32D64 = F32Tile<64, 2, 4, 64>;
+using F32D128 = F32Tile<128, 2, 4, 32>;
+
+constexpr double kLog2e = 1.44269504088896340736;  // 1 / ln 2
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+  return pa < pb + nb && pb < pa + na;
+}
+
+// Whether the current device is a gfx950; cached per device ordinal.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+hfa_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return HFA_ERR_NO_DEVICE;
+  }
+  if (dev >= kMaxDevices) return HFA_ERR_NO_DEVICE;
+  int st = g_arch_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return HFA_ERR_NO_DEVICE;
+    }
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? HFA_OK : HFA_ERR_NO_DEVICE;
+}
+
+// Raise the dynamic-LDS limit of a kernel once per process (per device the
+// attribute is a property of the function).
+template <class Kernel>
+hfa_status ensure_lds(Kernel kernel, int bytes, std::once_flag& flag, hipError_t& err) {
+  std::call_once(flag, [&] {
+    err = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  });
+  return err == hipSuccess ? HFA_OK : HFA_ERR_LAUNCH;
+}
+
+// Scale handling shared by both kernels: the kernels take a positive
+// log2-domain multiplier c2 = |scale| * log2(e) and fold the sign of the
+// scale into Q (q_mode = +1, -1, or 0 for scale == 0, where every score is 0).
+struct ScaleArgs {
+  double c2;
+  int q_mode;
+};
+ScaleArgs split_scale(float scale) {
+  if (scale == 0.0f) return {1.0, 0};
+  const double s = static_cast<double>(scale);
+  return {std::fabs(s) * kLog2e, s < 0 ? -1 : 1};
+}
+
+template <class T>
+hfa_status launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH,
+                       int64_t N, float scale, hipStream_t stream) {
+  static std::once_flag flag;
+  static hipError_t err = hipSuccess;
+  auto kernel = attn_fwd_bf16_kernel<T>;
+  if (ensure_lds(kernel, T::LDS_BYTES, flag, err) != HFA_OK) return HFA_ERR_LAUNCH;
+  const int64_t n_qt = (N + T::BR - 1) / T::BR;
+  const int64_t total = BH * n_qt;
+  if (total > INT_MAX) return HFA_ERR_SHAPE;
+  const ScaleArgs sa = split_scale(scale);
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(total)), dim3(T::NT), T::LDS_BYTES, stream,
+                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+                     static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, static_cast<int>(N),
+                     static_cast<int>(n_qt), static_cast<int>(total), static_cast<float>(sa.c2), sa.q_mode);
+  return hipGetLastError() == hipSuccess ? HFA_OK : HFA_ERR_LAUNCH;
+}
+
+template <class T>
+hfa_status launch_f32(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH,
+                      int64_t N, float scale, hipStream_t stream) {
+  static std::once_flag flag;
+  static hipError_t err = hipSuccess;
+  auto kernel = attn_fwd_f32_kernel<T>;
+  if (ensure_lds(kernel, T::LDS_BYTES, flag, err) != HFA_OK) return HFA_ERR_LAUNCH;
+  const int64_t n_qt = (N + T::BR - 1) / T::BR;
+  const int64_t total = BH * n_qt;
+  if (total > INT_MAX) return HFA_ERR_SHAPE;
+  const ScaleArgs sa = split_scale(scale);
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(total)), dim3(T::NT), T::LDS_BYTES, stream,
+                     static_cast<const float*>(q), static_cast<const float*>(k),
+                     static_cast<const float*>(v), static_cast<float*>(o), lse, static_cast<int>(N),
+                     static_cast<int>(n_qt), static_cast<int>(total), sa.c2, sa.q_mode);
+  return hipGetLastError() == hipSuccess ? HFA_OK : HFA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t hfa_block_rows(hfa_dtype dtype, int64_t d) {
+  if (dtype == HFA_BF16 && d == 128) return Bf16D128::BR;
+  if (dtype == HFA_BF16 && d == 64) return Bf16D64::BR;
+  if (dtype == HFA_F32 && d == 64) return F32D64::BR;
+  if (dtype == HFA_F32 && d == 128) return F32D128::BR;
+  return 0;
+}
+
+const char* hfa_status_str(hfa_status s) {
+  switch (s) {
+    case HFA_OK: return "ok";
+    case HFA_ERR_NULL: return "a required pointer is NULL";
+    case HFA_ERR_SHAPE: return "invalid shape: B, H, N must be >= 1 and N*d < 2^31";
+    case HFA_ERR_UNSUPPORTED: return "unsupported head dim (64 or 128) or dtype";
+    case HFA_ERR_SCALE: return "scale must be finite";
+    case HFA_ERR_ALIGN: return "q, k, v, o must be 16-byte aligned and lse 4-byte aligned";
+    case HFA_ERR_ALIAS: return "o or lse overlaps an input or each other";
+    case HFA_ERR_NO_DEVICE: return "no current gfx950 HIP device";
+    case HFA_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+hfa_status hfa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                        int64_t H, int64_t N, int64_t d, float scale, hfa_dtype dtype, void* stream) {
+  if (dtype != HFA_F32 && dtype != HFA_BF16) return HFA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return HFA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !o || !lse) return HFA_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return HFA_ERR_SHAPE;
+  if (N > INT_MAX / d) return HFA_ERR_SHAPE;
+  if (B > INT64_MAX / H) return HFA_ERR_SHAPE;
+  const int64_t BH = B * H;
+  if (BH > INT_MAX) return HFA_ERR_SHAPE;
+  if (!std::isfinite(scale)) return HFA_ERR_SCALE;
+  auto misaligned = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; };
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(lse, 4))
+    return HFA_ERR_ALIGN;
+  const size_t elt = dtype == HFA_F32 ? 4 : 2;
+  const size_t n_elems = static_cast<size_t>(BH) * static_cast<size_t>(N) * static_cast<size_t>(d);
+  const size_t bytes = n_elems * elt;
+  const size_t lse_bytes = static_cast<size_t>(BH) * static_cast<size_t>(N) * sizeof(float);
+  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes) ||
+      overlaps(lse, lse_bytes, q, bytes) || overlaps(lse, lse_bytes, k, bytes) ||
+      overlaps(lse, lse_bytes, v, bytes) || overlaps(lse, lse_bytes, o, bytes))
+    return HFA_ERR_ALIAS;
+
+  const hfa_status dev = check_device();
+  if (dev != HFA_OK) return dev;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == HFA_BF16) {
+    if (d == 128) return launch_bf16<Bf16D128>(q, k, v, o, lse, BH, N, scale, st);
+    return launch_bf16<Bf16D64>(q, k, v, o, lse, BH, N, scale, st);
+  }
+  if (d == 64) return launch_f32<F32D64>(q, k, v, o, lse, BH, N, scale, st);
+  return launch_f32<F32D128>(q, k, v, o, lse, BH, N, scale, st);
+}
+
+}  // extern "C"

@@ -1,0 +1,92 @@
+/* hfa.h -- C ABI of libhfa.so: exact attention forward on AMD MI355X (gfx950).
+ *
+ * The operation.  For every batch b and head h, with S = Q K^T * scale,
+ *
+ *     O   = softmax(S) V                    (row softmax over the keys)
+ *     LSE = log(sum_j exp(S[:, j]))         (natural log, per query row)
+ *
+ * i.e. "Attention(Q,K,V) = softmax(QK^T / sqrt(d_k)) V" as defined on the
+ * neuralmasteryai page "Hardware Acceleration & Custom Kernels", section 2
+ * ("FlashAttention: SRAM Tiling & Online Softmax"), computed the way that
+ * section describes: Q, K and V are cut into row tiles that live on chip, and
+ * the softmax is taken by the online normalisation identity (running max and
+ * running denominator, with the running output sums rescaled as each key tile
+ * arrives), so the N x N score matrix is never written to memory.  The
+ * TritonForge page ("Tiled FlashAttention-2" card) states the same property:
+ * O(N) memory, no N x N matrix materialised.  The log-sum-exp output is not on
+ * the pages; it is the running max plus the log of the running denominator.
+ *
+ * Precision.  HFA_F32: fp32 in and out; Q K^T is formed in fp64 on the matrix
+ * cores from the exactly widened fp32 inputs, exp2 and P V run in fp32, the
+ * log-sum-exp is combined in fp64.  HFA_BF16: bf16 in and out, matrix
+ * products on bf16 matrix cores with fp32 accumulation, softmax in fp32,
+ * P rounded to bf16 (round-to-nearest-even) for P V, O rounded to bf16 once.
+ *
+ * Ownership.  The caller owns every buffer; the library allocates nothing,
+ * keeps no state between calls and never holds an N x N buffer.  All pointers
+ * passed to hfa_attn_fwd are device pointers on the current HIP device.
+ *
+ * Errors.  Every argument is validated before any HIP call is made; on a
+ * validation error the call returns the status and leaves o and lse
+ * untouched.  The launch is asynchronous on `stream`: HFA_OK means the work
+ * was enqueued; faults during execution surface at the caller's next
+ * synchronisation.  The functions are thread-safe.
+ */
+#ifndef HFA_H
+#define HFA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HFA_F32 = 0,  /* fp32 (4-byte IEEE binary32) elements */
+  HFA_BF16 = 1  /* bf16 (2-byte, upper half of binary32) elements */
+} hfa_dtype;
+
+typedef enum {
+  HFA_OK = 0,
+  HFA_ERR_NULL = 1,        /* a required pointer is NULL */
+  HFA_ERR_SHAPE = 2,       /* B, H or N < 1, or the problem exceeds the index limits */
+  HFA_ERR_UNSUPPORTED = 3, /* head dim d not in {64, 128}, or dtype unknown */
+  HFA_ERR_SCALE = 4,       /* scale is NaN or infinite */
+  HFA_ERR_ALIGN = 5,       /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
+  HFA_ERR_ALIAS = 6,       /* o or lse overlaps q, k, v or each other */
+  HFA_ERR_NO_DEVICE = 7,   /* no HIP device is current, or it is not gfx950 */
+  HFA_ERR_LAUNCH = 8       /* the kernel launch itself failed */
+} hfa_status;
+
+/* Attention forward.
+ *
+ *   q, k, v  device, [B, H, N, d] contiguous row-major, element type `dtype`.
+ *            Read only; may alias each other.
+ *   o        device, [B, H, N, d] contiguous, element type `dtype`. Written once.
+ *   lse      device, [B, H, N] contiguous fp32, natural-log log-sum-exp of the
+ *            scaled scores of each query row.  Written once.
+ *   B, H, N  batch, heads, sequence length: each >= 1, N * d < 2^31.
+ *   d        head dimension: 64 or 128.
+ *   scale    multiplier of Q K^T (1/sqrt(d) for the usual attention); any finite
+ *            value, 0 included.
+ *   dtype    HFA_F32 or HFA_BF16, for q, k, v and o alike.
+ *   stream   a hipStream_t, passed as a pointer; NULL selects the null stream.
+ *
+ * Returns HFA_OK or one of the error codes above. */
+hfa_status hfa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                        hfa_dtype dtype, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* hfa_status_str(hfa_status s);
+
+/* Query rows owned by one workgroup of the kernel selected for (dtype, d),
+ * i.e. the row-tile height B_r of the tiling; 0 for an unsupported pair.
+ * Needs no device and makes no HIP call. */
+int64_t hfa_block_rows(hfa_dtype dtype, int64_t d);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HFA_H */

@@ -1,0 +1,130 @@
+"""The C-ABI boundary on the CPU: the library loads, exports what include/hfa.h
+declares, and rejects every invalid argument before making any HIP call.
+
+Fake device addresses are used; they are never dereferenced because each call
+here fails validation first.  The one call that passes validation (the
+no-device case) runs only where no GPU is visible.
+"""
+
+import re
+import subprocess
+from pathlib import Path
+
+import pytest
+import torch
+
+import fa2_fwd_amd as hfa
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "hfa.h"
+
+GOOD = dict(q=0x100000, k=0x200000, v=0x300000, o=0x400000, lse=0x500000)
+
+
+def _declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hfa_[a-z_0-9]+)\s*\(", text)))
+
+
+def _call(**kw):
+    a = dict(GOOD, B=1, H=1, N=128, d=64, scale=0.125, dtype=hfa.HFA_F32, stream=None)
+    a.update(kw)
+    return hfa.hfa_attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                            a["scale"], a["dtype"], a["stream"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = hfa.load_library()
+    declared = _declared_functions()
+    assert set(declared) == set(hfa.EXPORTED)
+    out = subprocess.run(["nm", "-D", "--defined-only", str(hfa.LIB_PATH)], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (hfa_\w+)", out))
+    for name in declared:
+        assert name in exported, f"{name} declared in hfa.h but not exported"
+        assert getattr(lib, name) is not None
+
+
+def test_library_is_gfx950_only(tmp_path):
+    # The device code sits in the .hip_fatbin section; list its offload targets.
+    fatbin = tmp_path / "fatbin.bin"
+    subprocess.run(["objcopy", f"--dump-section=.hip_fatbin={fatbin}", str(hfa.LIB_PATH), str(tmp_path / "x.so")],
+                   check=True)
+    out = subprocess.run(["/opt/rocm/llvm/bin/clang-offload-bundler", "--list", "--type=o", f"--input={fatbin}"],
+                         capture_output=True, text=True, check=True).stdout
+    targets = [t for t in out.split() if "amdgcn" in t]
+    assert targets and all(t.endswith("gfx950") for t in targets), out
+
+
+def test_status_strings_distinct():
+    codes = range(0, 9)
+    strs = [hfa.hfa_status_str(c) for c in codes]
+    assert len(set(strs)) == len(strs)
+    assert hfa.hfa_status_str(99) == "unknown status"
+
+
+def test_block_rows_table():
+    for dt in (hfa.HFA_F32, hfa.HFA_BF16):
+        for d in (64, 128):
+            br = hfa.hfa_block_rows(dt, d)
+            assert br > 0 and br % 16 == 0
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 96) == 0
+    assert hfa.hfa_block_rows(7, 64) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=2), hfa.HFA_ERR_UNSUPPORTED),
+    (dict(d=96), hfa.HFA_ERR_UNSUPPORTED),
+    (dict(d=256), hfa.HFA_ERR_UNSUPPORTED),
+    (dict(q=None), hfa.HFA_ERR_NULL),
+    (dict(k=None), hfa.HFA_ERR_NULL),
+    (dict(v=None), hfa.HFA_ERR_NULL),
+    (dict(o=None), hfa.HFA_ERR_NULL),
+    (dict(lse=None), hfa.HFA_ERR_NULL),
+    (dict(B=0), hfa.HFA_ERR_SHAPE),
+    (dict(H=0), hfa.HFA_ERR_SHAPE),
+    (dict(N=0), hfa.HFA_ERR_SHAPE),
+    (dict(N=-5), hfa.HFA_ERR_SHAPE),
+    (dict(N=2**31 // 64 + 1), hfa.HFA_ERR_SHAPE),
+    (dict(scale=float("nan")), hfa.HFA_ERR_SCALE),
+    (dict(scale=float("inf")), hfa.HFA_ERR_SCALE),
+    (dict(scale=float("-inf")), hfa.HFA_ERR_SCALE),
+    (dict(q=0x100008), hfa.HFA_ERR_ALIGN),
+    (dict(v=0x300004), hfa.HFA_ERR_ALIGN),
+    (dict(o=0x400002), hfa.HFA_ERR_ALIGN),
+    (dict(lse=0x500002), hfa.HFA_ERR_ALIGN),
+    (dict(o=0x100000 + 64), hfa.HFA_ERR_ALIAS),          # o overlaps q
+    (dict(lse=0x300000 + 16), hfa.HFA_ERR_ALIAS),        # lse overlaps v
+    (dict(lse=0x400000 + 1024), hfa.HFA_ERR_ALIAS),      # lse overlaps o
+])
+def test_validation_rejects_before_any_device_call(kw, status):
+    assert _call(**kw) == status
+
+
+def test_inputs_may_alias_each_other():
+    # q, k and v are read-only and may share memory; this must pass validation
+    # (it then stops at the device check on a GPU-less host).
+    if torch.cuda.is_available():
+        pytest.skip("would launch on a visible GPU with fake pointers")
+    assert _call(k=GOOD["q"], v=GOOD["q"]) == hfa.HFA_ERR_NO_DEVICE
+
+
+def test_no_device_reported():
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    for dt in (hfa.HFA_F32, hfa.HFA_BF16):
+        for d in (64, 128):
+            assert _call(dtype=dt, d=d) == hfa.HFA_ERR_NO_DEVICE
+
+
+def test_python_binding_value_errors():
+    q = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(ValueError):
+        hfa.attn_fwd(q, q, q)  # host tensors
+    with pytest.raises(ValueError):
+        hfa.attn_fwd(q, q[:, :, :4], q)
+    with pytest.raises(ValueError):
+        hfa.attn_fwd(q.double(), q.double(), q.double())
+    with pytest.raises(ValueError):
+        hfa.attn_fwd(q[0], q[0], q[0])

@@ -1,0 +1,211 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 CPU oracle.
+
+Tolerances:
+  fp32 -- max |gpu - oracle| <= 1e-5 on O and on LSE (the TritonForge page's
+          parity bound, atol = 1e-5, taken against the exact fp64 result).
+          Where half an fp32 ulp of the exact value exceeds 1e-5 (|LSE| >= 256,
+          reached only by the extra peaked case, never by the five evaluation
+          shapes) no fp32 output can meet 1e-5; there the bound is half an
+          ulp + 1e-6, i.e. correct rounding up to 1e-6 of computation error;
+  bf16 -- |gpu - oracle| <= 2e-2 + 1e-2 * |oracle| element-wise on O and LSE.
+The oracle reads the very host bytes that are copied to the device.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import fa2_fwd_amd as hfa
+import oracle
+from fa2_fwd_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+F32_ATOL = 1e-5
+BF16_ATOL, BF16_RTOL = 2e-2, 1e-2
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def run_gpu(q, k, v, scale):
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o, lse = hfa.attn_fwd(qd, kd, vd, scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+def run_oracle(q, k, v, scale, rows=None):
+    return oracle.attn_fwd(*(W.to_oracle_array(t) for t in (q, k, v)), scale, rows=rows)
+
+
+def f32_tolerance(ref):
+    """1e-5, or half an fp32 ulp of the exact value + 1e-6 where that is larger."""
+    half_ulp = np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64) / 2
+    return np.maximum(F32_ATOL, half_ulp + 1e-6)
+
+
+def assert_close(name, got_o, got_lse, ref_o, ref_lse, dtype):
+    assert np.isfinite(got_o).all(), f"{name}: non-finite O"
+    assert np.isfinite(got_lse).all(), f"{name}: non-finite LSE"
+    report = []
+    for what, g, r in (("O", got_o, ref_o), ("LSE", got_lse, ref_lse)):
+        err = np.abs(g - r)
+        tol = f32_tolerance(r) if dtype == "f32" else BF16_ATOL + BF16_RTOL * np.abs(r)
+        excess = err - tol
+        worst = np.unravel_index(np.argmax(excess), excess.shape)
+        report.append(f"max|d{what}|={err.max():.3e}")
+        assert excess.max() <= 0, f"{name}: {what} off by {err[worst]:.3e} (tol {np.broadcast_to(tol, err.shape)[worst]:.3e}) at {worst}"
+    _log(f"[parity] {name}: " + " ".join(report))
+
+
+def check_case(name, q, k, v, scale, dtype, rows=None):
+    _log(f"[parity] {name}")
+    go, gl = run_gpu(q, k, v, scale)
+    ro, rl = run_oracle(q, k, v, scale, rows)
+    if rows is not None:
+        go, gl = go[:, :, rows], gl[:, :, rows]
+    assert_close(name, go, gl, ro, rl, dtype)
+    return go, gl
+
+
+# ---- the five evaluation shapes --------------------------------------------
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_fp32_configs_full(cfg):
+    w = W.CONFIGS[cfg]
+    q, k, v = W.workload_inputs(w)
+    check_case(w.describe(), q, k, v, w.scale, w.dtype)
+
+
+@pytest.mark.parametrize("cfg", [4, 5])
+def test_bf16_configs_sampled_rows(cfg):
+    # Full shapes, same launch as the benchmark; the oracle checks a
+    # deterministic sample of query rows of every head (tile edges, middle,
+    # end, plus seeded random rows).
+    w = W.CONFIGS[cfg]
+    q, k, v = W.workload_inputs(w)
+    rows = W.sample_rows(w.N, 24, seed=1000 + cfg)
+    check_case(w.describe() + f" ({len(rows)} rows/head)", q, k, v, w.scale, w.dtype, rows=rows)
+
+
+# ---- awkward shapes: ragged tails, one row, tiny and odd N ------------------
+
+AWKWARD_N = [1, 2, 17, 63, 64, 65, 127, 129, 1000]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", AWKWARD_N)
+def test_awkward_shapes(dtype, d, N):
+    B, H = (1, 3) if N % 2 else (3, 1)
+    q, k, v = W.make_inputs(B, H, N, d, dtype, seed=N * 7 + d)
+    check_case(f"awkward {dtype} B={B} H={H} N={N} d={d}", q, k, v, 1.0 / math.sqrt(d), dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_long_ragged_sequence(dtype, d):
+    N = 4097
+    q, k, v = W.make_inputs(1, 2, N, d, dtype, seed=4097 + d, qk_mult=2.0 if dtype == "f32" else 1.0)
+    rows = W.sample_rows(N, 40, seed=d)
+    check_case(f"ragged {dtype} N={N} d={d}", q, k, v, 1.0 / math.sqrt(d), dtype, rows=rows)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_peaked_rows(dtype):
+    # Q and K x8: score standard deviation ~ 64 * scale; stresses the rescale.
+    q, k, v = W.make_inputs(2, 2, 700, 64, dtype, seed=77, qk_mult=8.0)
+    check_case(f"peaked {dtype}", q, k, v, 0.125, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("scale", [-0.125, 0.0, 0.01, 1.0])
+def test_other_scales(dtype, scale):
+    q, k, v = W.make_inputs(1, 2, 300, 64, dtype, seed=int(abs(scale) * 1000) + 5)
+    check_case(f"scale={scale} {dtype}", q, k, v, scale, dtype)
+
+
+# ---- invariants on device output --------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_invariants_on_device(dtype, d):
+    B, H, N = 1, 2, 333
+    q, k, v = W.make_inputs(B, H, N, d, dtype, seed=5, qk_mult=4.0)
+    tol = 1e-5 if dtype == "f32" else 2e-2
+    # constant V -> that constant
+    c = v[:, :, :1].expand(B, H, N, d).contiguous()
+    o, _ = run_gpu(q, k, c, 1.0 / math.sqrt(d))
+    assert np.abs(o - c.double().numpy()).max() <= tol
+    # identical keys -> mean of V, LSE = scale q.k + ln N
+    kk = k[:, :, :1].expand(B, H, N, d).contiguous()
+    o, lse = run_gpu(q, kk, v, 0.125)
+    mean_v = v.double().mean(dim=2, keepdim=True).expand(B, H, N, d).numpy()
+    assert np.abs(o - mean_v).max() <= tol
+    qk = torch.einsum("bhnd,bhd->bhn", q.double(), kk[:, :, 0].double()).numpy()
+    ref_lse = 0.125 * qk + math.log(N)
+    lse_tol = f32_tolerance(ref_lse) if dtype == "f32" else BF16_ATOL + BF16_RTOL * np.abs(ref_lse)
+    assert np.all(np.abs(lse - ref_lse) <= lse_tol)
+    # scale 0 -> mean of V, LSE = ln N
+    o, lse = run_gpu(q, k, v, 0.0)
+    assert np.abs(o - mean_v).max() <= tol
+    assert np.abs(lse - math.log(N)).max() <= 1e-5
+
+
+# ---- engineering checks -----------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_bitwise_deterministic(dtype):
+    q, k, v = W.make_inputs(2, 4, 1500, 128 if dtype == "bf16" else 64, dtype, seed=9)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o1, l1 = hfa.attn_fwd(qd, kd, vd)
+    o2, l2 = hfa.attn_fwd(qd, kd, vd)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_writes_stay_in_bounds(dtype):
+    # O and LSE live inside larger guard buffers; nothing outside may change.
+    B, H, N, d = 1, 3, 130, 64
+    q, k, v = W.make_inputs(B, H, N, d, dtype, seed=11)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    n = B * H * N * d
+    guard = 4096
+    obuf = torch.full((n + 2 * guard,), 7.0, dtype=qd.dtype, device=dev)
+    lbuf = torch.full((B * H * N + 2 * guard,), 7.0, dtype=torch.float32, device=dev)
+    o = obuf[guard:guard + n].view(B, H, N, d)
+    lse = lbuf[guard:guard + B * H * N].view(B, H, N)
+    hfa.attn_fwd(qd, kd, vd, out=o, lse=lse)
+    torch.cuda.synchronize()
+    for buf in (obuf, lbuf):
+        assert torch.all(buf[:guard] == 7.0) and torch.all(buf[-guard:] == 7.0)
+    ro, rl = run_oracle(q, k, v, 1.0 / math.sqrt(d))
+    assert_close("guarded", o.float().cpu().double().numpy(), lse.cpu().double().numpy(), ro, rl, dtype)
+
+
+def test_side_stream():
+    q, k, v = W.make_inputs(1, 2, 256, 128, "bf16", seed=12)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o, lse = hfa.attn_fwd(qd, kd, vd)
+    s.synchronize()
+    ro, rl = run_oracle(q, k, v, 1.0 / math.sqrt(128))
+    assert_close("side stream", o.float().cpu().double().numpy(), lse.cpu().double().numpy(), ro, rl, "bf16")
+
+
+def test_status_on_device():
+    # a validation error on a real device still returns before launching
+    q = torch.zeros(1, 1, 16, 96, device="cuda:0")
+    with pytest.raises(hfa.HfaError) as ei:
+        hfa.attn_fwd(q, q, q)
+    assert ei.value.status == hfa.HFA_ERR_UNSUPPORTED
