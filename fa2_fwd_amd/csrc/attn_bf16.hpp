@@ -1,30 +1,46 @@
 // bf16 attention forward for gfx950: O = softmax(Q K^T * scale) V and its
 // log-sum-exp, computed tile by tile with the online normalisation identity
 // (neuralmasteryai "Hardware Acceleration & Custom Kernels", section 2,
-// steps 1-2): one workgroup owns a block of query rows held in registers,
-// K/V tiles stream through double-buffered LDS, and the running max, running
-// denominator and running output sums are rescaled as each key tile arrives,
-// so no score ever reaches HBM.
+// steps 1-2): each wave owns 32 query rows held in registers, K/V tiles
+// stream through double-buffered LDS, and the running max, running
+// denominator and running output sums are rescaled as key tiles arrive, so
+// no score ever reaches HBM.
 //
 // Matrix-core mapping (v_mfma_f32_32x32x16_bf16, fp32 accumulate):
 //
 //  * Scores are formed transposed, S^T = K Q^T: the A operand is 32 key rows
-//    of K (from LDS), the B operand is 32 query rows of Q (registers).  In
-//    the 32x32 accumulator each lane then owns ONE query (lane % 32) and 16 of
-//    the 32 keys, so the row max and row sum are lane-local plus one exchange
-//    with the lane 32 apart.
+//    of K (from LDS), the B operand is the wave's 32 query rows (registers).
+//    In the 32x32 accumulator each lane then owns ONE query (lane % 32) and 16
+//    of the 32 keys, so the row max and row sum are lane-local plus one
+//    exchange with the lane 32 apart (v_permlane32_swap).
 //  * The keys fed into the A operand are permuted (row i of the MFMA reads
-//    key pi(i)) so that accumulator registers r = 0..7 / 8..15 of the lane
-//    half h hold the 8 consecutive keys 16*c + 8h + (r % 8) of chunk c.
-//    That is exactly the B-operand layout of the next product, so P never
-//    leaves registers:
+//    key pi(i)) so that accumulator registers r = 0..7 / 8..15 of lane half h
+//    hold the 8 consecutive keys 16*c + 8h + (r % 8) of chunk c.  That is
+//    exactly the B-operand layout of the next product, so P never leaves
+//    registers.
 //  * O^T = V^T P^T: the A operand is V^T (8 consecutive keys of one head-dim
 //    column per lane), read from the row-major V tile with the gfx950
 //    transposing LDS load (ds_read_b64_tr_b16, 4 keys x 16 columns per 16
 //    lanes); the B operand is P rounded to bf16.  Each lane's accumulator
-//    again belongs to its own query, so the per-row rescale is a lane-local
-//    multiply.
+//    again belongs to its own query, so the per-row rescale is lane-local.
+//
+// Schedule ("ping-pong").  The 8 waves form two groups, one wave of each per
+// SIMD, offset by half a tile.  A wave alternates an MFMA phase (S_j = K_j
+// Q^T together with the previous tile's P_{j-1} V_{j-1}: software pipelined)
+// and a VALU phase (softmax of S_j, rescale, P_j).  Workgroup barriers
+// separate the phases, and since the second group enters the loop one
+// barrier later, in every interval one wave of each SIMD issues matrix-core
+// work while the other runs its softmax on the vector unit.
+//
+// LDS tiles: K_t and V_t live in buffer t % 4 of two rings.  Group 0 requests
+// K_{j+2} and group 1 requests V_{j+2} from HBM straight into LDS at the start
+// of their MFMA phase j; each group waits for its own requests just before
+// the barrier preceding a tile's first reader.  Across the barrier intervals
+// a buffer is refilled only after both groups finished reading its previous
+// tile, and every tile has three to five intervals to arrive.
 #pragma once
+
+#include <type_traits>
 
 #include "common.hpp"
 
@@ -34,7 +50,7 @@ template <int D_, int QB_, int NW_>
 struct Bf16Tile {
   static constexpr int D = D_;        // head dim (64 or 128)
   static constexpr int QB = QB_;      // 32-query blocks per wave
-  static constexpr int NW = NW_;      // waves per workgroup
+  static constexpr int NW = NW_;      // waves per workgroup (two ping-pong groups)
   static constexpr int KT = 64;       // keys per K/V tile
   static constexpr int WQ = 32 * QB;  // queries per wave
   static constexpr int BR = WQ * NW;  // queries per workgroup (row-tile height)
@@ -42,19 +58,83 @@ struct Bf16Tile {
   static constexpr int ROWB = D * 2;  // bytes per K or V row in LDS (XOR-swizzled, unpadded)
   static constexpr int TILEB = KT * ROWB;
   static constexpr int CH = D / 8;             // 16-byte chunks per row
-  static constexpr int LOADS = KT * CH / NT;   // chunks per thread per tile per tensor
-  static constexpr int LDS_BYTES = 2 * 2 * TILEB;  // two buffers of (K tile, V tile)
-  static_assert((KT * CH) % NT == 0, "tile chunks must divide evenly over the threads");
-  static_assert(CH >= 8, "row must span all eight 16-byte bank groups");
+  static constexpr int NBUF = 4;               // LDS ring depth, tiles per tensor
+  static constexpr int AHEAD = 2;              // tiles requested ahead of their first use
+  static constexpr int LD = TILEB / (4 * 64 * 16);  // 16-byte loads per lane per tile (one group of 4 waves)
+  static constexpr int LDS_BYTES = 2 * NBUF * TILEB;  // K ring and V ring
+  static_assert(LD >= 1 && TILEB % (4 * 64 * 16) == 0, "a tile must split into whole load instructions");
+  static_assert(CH == 8 || CH == 16, "swizzles are defined for d = 64 and d = 128");
+  static_assert(NW == 8, "the ping-pong schedule pairs two waves per SIMD");
 };
 
-// K rows: eight consecutive lanes of an S MFMA read the rows pi(0..7) =
-// {0,1,2,3,8,9,10,11} (+4, +16, +20 for the other lane octets); this XOR puts
-// those eight 16-byte reads on eight different bank groups.
-__device__ __forceinline__ int k_swz(int row) { return (row & 3) | ((row >> 1) & 4); }
-// V rows: one transposing read covers 4 consecutive rows x 32 bytes per 16
-// lanes; XOR by an even value per row spreads the 4 rows over all banks.
-__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 1; }
+// LDS serves 16 lanes x 16 bytes per clock (64 banks); a 16-byte access
+// occupies one of 16 "bank groups" given by (byte address / 16) mod 16.  The
+// swizzles below XOR the 16-byte chunk index within a row (CH chunks per row)
+// so that every group of lanes served together hits 16 different groups:
+//
+// K rows: lanes 0..15 (and 16..31) of an S MFMA read 16 different rows at the
+// same logical chunk; writes put 16 consecutive chunks of one row (CH = 16) or
+// of two rows (CH = 8) on 16 lanes.
+template <int CH>
+__device__ __forceinline__ int k_swz(int row) {
+  return CH == 16 ? (row & 15) : ((row >> 1) & 7);
+}
+// V rows: one transposing read covers 4 consecutive rows x 4 chunks per 32
+// lanes; the XOR moves whole 4-chunk blocks so the four rows land apart.
+template <int CH>
+__device__ __forceinline__ int v_swz(int row) {
+  return CH == 16 ? ((row & 3) << 2) : (((row >> 1) & 1) << 2);
+}
+
+#ifndef HFA_SCHED_GROUPS
+#define HFA_SCHED_GROUPS 1
+#endif
+#ifndef HFA_PF
+#define HFA_PF 2
+#endif
+
+// Largest growth of the running max (log2 units) absorbed without rescaling.
+constexpr float kRescaleLog2 = 8.0f;
+
+// Workgroup barrier that waits only for this wave's LDS operations: global
+// loads issued before it stay in flight.  The memory clobber keeps the
+// compiler from moving any memory access across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4): lane l
+// reads base + voff(l) and writes LDS bytes [lds + 16 l, lds + 16 l + 16).
+// base and lds must be wave-uniform.  Issued through inline assembly so that
+// the compiler does not make every later LDS read wait for it; completion is
+// ordered explicitly with vmcnt_wait and the workgroup barriers.
+#ifndef HFA_DMA_ASM
+#define HFA_DMA_ASM 1
+#endif
+__device__ __forceinline__ void dma16(const char* base, int voff, char* lds) {
+#if HFA_DMA_ASM
+  const unsigned lds_addr = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void*)lds));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff), "s"(base)
+               : "memory", "m0");
+#else
+  __builtin_amdgcn_global_load_lds(base + voff, (lds_void*)lds, 16, 0, 0);
+#endif
+}
+
+// Rescale of the output accumulators: 0 = every tile (alpha is 1 unless the
+// running max moved), 1 = only in a wave-uniform branch when some lane's max
+// moved by more than kRescaleLog2.
+#ifndef HFA_RESCALE_MODE
+#define HFA_RESCALE_MODE 1
+#endif
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void vmcnt_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 template <class T>
 __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
@@ -63,9 +143,13 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
     int q_mode) {
   constexpr int D = T::D, QB = T::QB, KT = T::KT, ROWB = T::ROWB, TILEB = T::TILEB;
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* const kbuf = smem;                    // K ring: NBUF tile buffers
+  char* const vbuf = smem + T::NBUF * TILEB;  // V ring: NBUF tile buffers
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in scalar registers
+  const int grp = wave >> 2;  // ping-pong group; waves w and w + 4 share a SIMD
   const int i32 = lane & 31, hh = lane >> 5;
 
   const int tile = xcd_remap(blockIdx.x, total_wg);
@@ -98,12 +182,12 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   // S MFMA row i32 reads key pi(i32) of each 32-key block.
   const int a8 = i32 >> 3, e4 = (i32 >> 2) & 1, b4 = i32 & 3;
   const int krow = 16 * (a8 >> 1) + 8 * e4 + 4 * (a8 & 1) + b4;
-  const int kswz = k_swz(krow);
+  const int kswz = k_swz<T::CH>(krow);
   // Transposing V read: in each 16-lane group, lane l16 reads row 4u + l16/4 of
   // the group's 4 rows at columns 16*g16 + 4*(l16 % 4) .. +3 of the 32-column block.
   const int l16 = lane & 15, g16 = (lane >> 4) & 1;
   const int vrow = 8 * hh + (l16 >> 2);
-  const int vswz = v_swz(vrow);
+  const int vswz = v_swz<T::CH>(vrow);
   const int vch = 2 * g16 + ((l16 & 3) >> 1);
   const int vin = (l16 & 1) * 8;
 
@@ -119,69 +203,133 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
       for (int r = 0; r < 16; ++r) acc[qb][n][r] = 0.0f;
   }
 
-  // ---- K/V staging: global -> registers -> LDS (swizzled), double-buffered.
-  u32x4 kreg[T::LOADS], vreg[T::LOADS];
-  auto stage_load = [&](int j) {
-#pragma unroll
-    for (int u = 0; u < T::LOADS; ++u) {
-      const int idx = tid + u * T::NT;
-      const int row = idx / T::CH, ch = idx % T::CH;
-      const int key = j * KT + row;
-      u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-      if (key < N) {
-        kx = *reinterpret_cast<const u32x4*>(Kh + static_cast<size_t>(key) * D + ch * 8);
-        vx = *reinterpret_cast<const u32x4*>(Vh + static_cast<size_t>(key) * D + ch * 8);
-      }
-      kreg[u] = kx;
-      vreg[u] = vx;
-    }
-  };
-  auto stage_store = [&](int buf) {
-    char* kt = smem + buf * 2 * TILEB;
-    char* vt = kt + TILEB;
-#pragma unroll
-    for (int u = 0; u < T::LOADS; ++u) {
-      const int idx = tid + u * T::NT;
-      const int row = idx / T::CH, ch = idx % T::CH;
-      lds_store16(kt, row * ROWB + ((ch ^ k_swz(row)) << 4), kreg[u]);
-      lds_store16(vt, row * ROWB + ((ch ^ v_swz(row)) << 4), vreg[u]);
-    }
-  };
-
   const int ntiles = (N + KT - 1) / KT;
-  stage_load(0);
-  stage_store(0);
-  __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) stage_load(j + 1);
-    const char* kt = smem + buf * 2 * TILEB;
-    const char* vt = kt + TILEB;
+  // ---- K/V streaming: HBM -> LDS directly (global_load_lds_dwordx4), no
+  // registers.  Group 0 streams the K tiles, group 1 the V tiles, each into a
+  // ring of NBUF tile buffers (tile t in buffer t % NBUF), AHEAD tiles before
+  // first use.  One load instruction writes 64 consecutive 16-byte LDS chunks
+  // in lane order, so the XOR swizzle is realised by choosing each lane's
+  // source chunk.  Keys past the end are clamped to the last row: their
+  // scores are masked to -inf and their weights are exactly zero.
+  const int wig = wave & 3;  // wave within its group
+  const __bf16* const stream_src = grp == 0 ? Kh : Vh;
+  char* const stream_ring = grp == 0 ? kbuf : vbuf;
+  auto issue_tile = [&](int t) {
+    if (t >= ntiles) return;
+    char* dst = stream_ring + (t % T::NBUF) * TILEB;
+    const char* tile_src = reinterpret_cast<const char*>(stream_src + static_cast<size_t>(t) * KT * D);
+    const bool full = (t + 1) * KT <= N;  // uniform: only the last tile can be ragged
+#pragma unroll
+    for (int u = 0; u < T::LD; ++u) {
+      const int pos = (wig * T::LD + u) * 64 + lane;  // 16-byte chunk position within the tile
+      const int row = pos / T::CH, phys = pos % T::CH;
+      const int ch = phys ^ (grp == 0 ? k_swz<T::CH>(row) : v_swz<T::CH>(row));
+      const int src_row = full ? row : min(row, N - 1 - t * KT);
+      dma16(tile_src, (src_row * D + ch * 8) * 2, dst + (wig * T::LD + u) * 1024);
+    }
+  };
 
-    // ---- S^T = K Q^T for this tile (fp32 accumulators)
-    f32x16 s[QB][KT / 32];
+  // ---- matrix-core work of one interval: S_j = K_j Q^T and, when with_pv,
+  // acc += V_{j-1}^T P_{j-1}^T.  The 2 x (D/16) score MFMAs and the
+  // (KT/16) x (D/32) output MFMAs are issued as one interleaved sequence of
+  // steps (one of each per step, on independent accumulators), with each
+  // step's LDS operands requested PF steps ahead, so neither the matrix-core
+  // dependency latency nor the LDS latency is exposed.
+  f32x16 s[QB][KT / 32];
+  bf16x8 pf[QB][KT / 16];
+  constexpr int SSTEPS = (KT / 32) * (D / 16);  // score MFMAs per tile (per query block)
+  constexpr int VSTEPS = (KT / 16) * (D / 32);  // output MFMAs per tile (per query block)
+  static_assert(SSTEPS == VSTEPS, "score and output products have the same MFMA count");
+  constexpr int STEPS = SSTEPS;
+  constexpr int PF = HFA_PF;  // prefetch distance in steps
+  auto k_off = [&](int i) {  // step i: key block i % 2, d-step i / 2
+    const int kb = i % (KT / 32), t = i / (KT / 32);
+    return (kb * 32 + krow) * ROWB + (((2 * t + hh) ^ kswz) << 4);
+  };
+  auto v_off = [&](int i) {  // step i: column block i % (D/32), key chunk i / (D/32)
+    const int n = i % (D / 32), c = i / (D / 32);
+    return (16 * c + vrow) * ROWB + (((4 * n + vch) ^ vswz) << 4) + vin;
+  };
+  auto mfma_phase = [&](int j, auto with_pv_tag) {
+    constexpr bool with_pv = decltype(with_pv_tag)::value;
+    const char* kt = kbuf + (j % T::NBUF) * TILEB;
+    const char* vt = vbuf + ((j + T::NBUF - 1) % T::NBUF) * TILEB;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < KT / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.0f;
+    u32x4 kq[PF + 1];
+    s16x4 vlo[PF + 1], vhi[PF + 1];
 #pragma unroll
-    for (int kb = 0; kb < KT / 32; ++kb) {
-#pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        const u32x4 kf = lds_load16(kt, (kb * 32 + krow) * ROWB + (((2 * t + hh) ^ kswz) << 4));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, kf), __builtin_bit_cast(bf16x8, qf[qb][t]), s[qb][kb], 0, 0, 0);
+    for (int i = 0; i < PF; ++i) {
+      kq[i] = lds_load16(kt, k_off(i));
+      if (with_pv) {
+        vlo[i] = lds_read_tr16(vt, v_off(i));
+        vhi[i] = lds_read_tr16(vt, v_off(i) + 4 * ROWB);
       }
     }
+#pragma unroll
+    for (int i = 0; i < STEPS; ++i) {
+      if (i + PF < STEPS) {
+        kq[(i + PF) % (PF + 1)] = lds_load16(kt, k_off(i + PF));
+        if (with_pv) {
+          vlo[(i + PF) % (PF + 1)] = lds_read_tr16(vt, v_off(i + PF));
+          vhi[(i + PF) % (PF + 1)] = lds_read_tr16(vt, v_off(i + PF) + 4 * ROWB);
+        }
+      }
+      const int kb = i % (KT / 32), t = i / (KT / 32);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kq[i % (PF + 1)]),
+                                                            __builtin_bit_cast(bf16x8, qf[qb][t]), s[qb][kb], 0, 0, 0);
+      if (with_pv) {
+        const int n = i % (D / 32), c = i / (D / 32);
+        const bf16x8 vf = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(vlo[i % (PF + 1)], vhi[i % (PF + 1)], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          acc[qb][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][c], acc[qb][n], 0, 0, 0);
+      }
+    }
+#if HFA_SCHED_GROUPS
+    // Pin the order: the HBM prefetch loads first, then per step the operand
+    // reads of a later step followed by that step's matrix-core instructions.
+    __builtin_amdgcn_sched_group_barrier(0x020, T::LD, 0);  // VMEM reads
+    __builtin_amdgcn_sched_group_barrier(0x100, PF * (with_pv ? 3 : 1), 0);  // DS reads
+#pragma unroll
+    for (int i = 0; i < STEPS; ++i) {
+      if (i + PF < STEPS) __builtin_amdgcn_sched_group_barrier(0x100, with_pv ? 3 : 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, (with_pv ? 2 : 1) * QB, 0);  // MFMA
+    }
+#endif
+  };
+  // final output product of the last tile, without scores
+  auto mfma_pv_only = [&](int j) {
+    const char* vt = vbuf + (j % T::NBUF) * TILEB;
+#pragma unroll
+    for (int i = 0; i < STEPS; ++i) {
+      const int n = i % (D / 32), c = i / (D / 32);
+      const s16x4 lo = lds_read_tr16(vt, v_off(i));
+      const s16x4 hi = lds_read_tr16(vt, v_off(i) + 4 * ROWB);
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        acc[qb][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][c], acc[qb][n], 0, 0, 0);
+    }
+  };
 
-    // ---- keys past the end of the sequence get score -inf (weight 0)
+  // ---- vector work of one interval: online softmax update of tile j.
+  // The running max only moves when it would grow by more than kRescaleLog2
+  // (log2 units) for some lane of the wave: a stale max keeps every
+  // p <= 2^kRescaleLog2, which the fp32 sums and the bf16 P represent with
+  // unchanged relative precision, and the final division by the denominator
+  // removes it exactly.  The rescale is then a rare, wave-uniform branch.
+  auto softmax = [&](int j) {
     const int key0 = j * KT;
-    if (key0 + KT > N) {
+    if (key0 + KT > N) {  // keys past the end of the sequence get score -inf (weight 0)
 #pragma unroll
       for (int kb = 0; kb < KT / 32; ++kb)
 #pragma unroll
@@ -192,8 +340,6 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
             for (int qb = 0; qb < QB; ++qb) s[qb][kb][r] = -INFINITY;
         }
     }
-
-    // ---- online softmax update: running max, rescale factor, probabilities
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float mx = -INFINITY;
@@ -202,49 +348,83 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
       mx = max_xor32(mx);
-      const float m_new = fmaxf(m_run[qb], mx);
-      const float alpha = exp2_hw((m_run[qb] - m_new) * c2);  // 0 on the first tile
-      const float mc = m_new * c2;
+      const float m_cand = fmaxf(m_run[qb], mx);
+      const bool grow = (m_cand - m_run[qb]) * c2 > kRescaleLog2;  // always true on the first tile
+#if HFA_RESCALE_MODE == 0
+      // unconditional: straight-line code, alpha == 1 unless the max moved
+      {
+        const float m_new = grow ? m_cand : m_run[qb];
+        const float alpha = exp2_hw((m_run[qb] - m_new) * c2);  // 0 on the first tile, 1 if kept
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n) acc[qb][n] *= alpha;
+        m_run[qb] = m_new;
+      }
+#else
+      if (__any(grow)) {
+        const float m_new = grow ? m_cand : m_run[qb];
+        const float alpha = exp2_hw((m_run[qb] - m_new) * c2);  // 0 on the first tile, 1 if kept
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n) acc[qb][n] *= alpha;
+        m_run[qb] = m_new;
+      }
+#endif
+      const float mc = m_run[qb] * c2;
       float ts = 0.0f;
 #pragma unroll
-      for (int kb = 0; kb < KT / 32; ++kb)
+      for (int c = 0; c < KT / 16; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = exp2_hw(fmaf(s[qb][kb][r], c2, -mc));
-          s[qb][kb][r] = p;
+        for (int e = 0; e < 8; ++e) {
+          const float p = exp2_hw(fmaf(s[qb][c >> 1][8 * (c & 1) + e], c2, -mc));
           ts += p;
+          pf[qb][c][e] = static_cast<__bf16>(p);
         }
-      l_run[qb] = l_run[qb] * alpha + ts;
-      m_run[qb] = m_new;
-#pragma unroll
-      for (int n = 0; n < D / 32; ++n)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[qb][n][r] *= alpha;
+      l_run[qb] += ts;
     }
+  };
 
-    // ---- O^T += V^T P^T, 16 keys per MFMA
-#pragma unroll
-    for (int c = 0; c < KT / 16; ++c) {
-      bf16x8 pf[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[qb][e] = static_cast<__bf16>(s[qb][c >> 1][8 * (c & 1) + e]);
-#pragma unroll
-      for (int n = 0; n < D / 32; ++n) {
-        const int base = (16 * c + vrow) * ROWB + (((4 * n + vch) ^ vswz) << 4) + vin;
-        const s16x4 lo = lds_read_tr16(vt, base);
-        const s16x4 hi = lds_read_tr16(vt, base + 4 * ROWB);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          acc[qb][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb], acc[qb][n], 0, 0, 0);
-      }
-    }
+  // Wait until this group's request for tile t is complete.  Requests go
+  // out in tile order and only for tiles < ntiles, so the number that may
+  // still be in flight is LD times the number of tiles requested after t.
+  auto wait_tile = [&](int t, int newest) {
+    const int after = min(newest, ntiles - 1) - t;
+    static_assert(T::AHEAD == 2, "wait_tile covers up to two newer tiles");
+    if (after <= 0)
+      vmcnt_wait<0>();
+    else if (after == 1)
+      vmcnt_wait<T::LD>();
+    else
+      vmcnt_wait<2 * T::LD>();
+  };
 
-    if (j + 1 < ntiles) stage_store(buf ^ 1);
-    __syncthreads();
-  }
+  // ---- prologue: the first AHEAD tiles of each stream; K_0 must be in LDS
+  // before group 0's first MFMA phase.
+#pragma unroll
+  for (int t = 0; t < T::AHEAD; ++t) issue_tile(t);
+  if (grp == 0) wait_tile(0, T::AHEAD - 1);
+  lds_barrier();
+  if (grp == 1) lds_barrier();  // group 1 runs half a tile behind
+
+  // One tile: MFMA phase (request tile j + AHEAD of this group's stream,
+  // scores of tile j, P V of tile j - 1), then VALU phase (softmax of tile j).
+  // Tile 0 is peeled off so that the accumulator flows straight through the
+  // loop body (no path around the output MFMAs).
+  auto tile_step = [&](int j, auto with_pv_tag) {
+    issue_tile(j + T::AHEAD);
+    mfma_phase(j, with_pv_tag);
+    // V_j is first read in the next interval (group 0's MFMA phase j + 1).
+    if (grp == 1) wait_tile(j, j + T::AHEAD);
+    lds_barrier();
+    softmax(j);
+    // K_{j+1} is first read in the next interval (group 0's MFMA phase j + 1).
+    if (grp == 0) wait_tile(j + 1, j + T::AHEAD);
+    lds_barrier();
+  };
+  tile_step(0, std::false_type{});
+  for (int j = 1; j < ntiles; ++j) tile_step(j, std::true_type{});
+  mfma_pv_only(ntiles - 1);
+  if (grp == 0) lds_barrier();  // both groups execute the same number of barriers
 
   // ---- epilogue: normalise, round to bf16, one write of O and of LSE
 #pragma unroll
@@ -264,7 +444,8 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
           *reinterpret_cast<bf16x4*>(orow + 32 * n + 8 * a + 4 * hh) = o4;
         }
       if (hh == 0) {
-        const double lse2 = static_cast<double>(m_run[qb]) * static_cast<double>(c2) + log2(static_cast<double>(l_tot));
+        const double lse2 =
+            static_cast<double>(m_run[qb]) * static_cast<double>(c2) + log2(static_cast<double>(l_tot));
         LSE[static_cast<size_t>(bh) * N + row] = static_cast<float>(lse2 * kLn2);
       }
     }

@@ -9,7 +9,7 @@
 #include <cstring>
 #include <mutex>
 
-#include "../../include/hfa.h"
+#include "hfa.h"
 #include "attn_bf16.hpp"
 #include "attn_f32.hpp"
 
@@ -17,11 +17,24 @@ namespace {
 
 using namespace hfa;
 
-// Tile configurations, one per (dtype, head dim).
-using Bf16D128 = Bf16Tile<128, 1, 4>;
-using Bf16D64 = Bf16Tile<64, 1, 4>;
-using F32D64 = F32Tile<64, 2, 4, 64>;
-using F32D128 = F32Tile<128, 2, 4, 32>;
+// Tile configurations, one per (dtype, head dim).  The macros exist so that
+// a tile sweep can build variants with -D; the defaults are the tuned choice.
+#ifndef HFA_BF16_D128_TILE
+#define HFA_BF16_D128_TILE 1, 8
+#endif
+#ifndef HFA_BF16_D64_TILE
+#define HFA_BF16_D64_TILE 1, 8
+#endif
+#ifndef HFA_F32_D64_TILE
+#define HFA_F32_D64_TILE 2, 4, 64
+#endif
+#ifndef HFA_F32_D128_TILE
+#define HFA_F32_D128_TILE 2, 4, 32
+#endif
+using Bf16D128 = Bf16Tile<128, HFA_BF16_D128_TILE>;
+using Bf16D64 = Bf16Tile<64, HFA_BF16_D64_TILE>;
+using F32D64 = F32Tile<64, HFA_F32_D64_TILE>;
+using F32D128 = F32Tile<128, HFA_F32_D128_TILE>;
 
 constexpr double kLog2e = 1.44269504088896340736;  // 1 / ln 2
 
