@@ -32,12 +32,13 @@
 // barrier later, in every interval one wave of each SIMD issues matrix-core
 // work while the other runs its softmax on the vector unit.
 //
-// LDS tiles: K_t and V_t live in buffer t % 4 of two rings.  Group 0 requests
-// K_{j+2} and group 1 requests V_{j+2} from HBM straight into LDS at the start
-// of their MFMA phase j; each group waits for its own requests just before
-// the barrier preceding a tile's first reader.  Across the barrier intervals
-// a buffer is refilled only after both groups finished reading its previous
-// tile, and every tile has three to five intervals to arrive.
+// LDS tiles: K_t and V_t live in buffer t % 4 of two rings filled straight
+// from HBM.  In its VALU phase j, group 0 requests K_{j+3} and group 1
+// requests V_{j+3}; each waits for its own earlier requests (K_{j+2},
+// respectively V_{j+1}) just before the barrier, so that in the next VALU
+// phase both groups can already read the operands of their next MFMA phase.
+// Across the barrier intervals a buffer is refilled only after both groups
+// finished reading its previous tile.
 #pragma once
 
 #include <type_traits>
@@ -59,7 +60,7 @@ struct Bf16Tile {
   static constexpr int TILEB = KT * ROWB;
   static constexpr int CH = D / 8;             // 16-byte chunks per row
   static constexpr int NBUF = 4;               // LDS ring depth, tiles per tensor
-  static constexpr int AHEAD = 2;              // tiles requested ahead of their first use
+  static constexpr int AHEAD = 3;              // tiles of each stream requested ahead
   static constexpr int LD = TILEB / (4 * 64 * 16);  // 16-byte loads per lane per tile (one group of 4 waves)
   static constexpr int LDS_BYTES = 2 * NBUF * TILEB;  // K ring and V ring
   static_assert(LD >= 1 && TILEB % (4 * 64 * 16) == 0, "a tile must split into whole load instructions");
@@ -100,7 +101,9 @@ constexpr float kRescaleLog2 = 8.0f;
 // loads issued before it stay in flight.  The memory clobber keeps the
 // compiler from moving any memory access across it.
 __device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);  // no instruction (MFMAs included) crosses the barrier
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // One 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4): lane l
@@ -113,20 +116,20 @@ __device__ __forceinline__ void lds_barrier() {
 #endif
 __device__ __forceinline__ void dma16(const char* base, int voff, char* lds) {
 #if HFA_DMA_ASM
-  const unsigned lds_addr = static_cast<unsigned>(reinterpret_cast<uintptr_t>((lds_void*)lds));
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff), "s"(base)
+  // readfirstlane returns int: every half goes through uint32_t before it is
+  // widened, so the low half is never sign-extended into the high word.
+  const uint32_t lds_addr = static_cast<uint32_t>(
+      __builtin_amdgcn_readfirstlane(static_cast<int>(reinterpret_cast<uintptr_t>((lds_void*)lds))));
+  const uint64_t b = reinterpret_cast<uintptr_t>(base);
+  const uint32_t b_lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b))));
+  const uint32_t b_hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b >> 32))));
+  const uint64_t sbase = (static_cast<uint64_t>(b_hi) << 32) | static_cast<uint64_t>(b_lo);
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff), "s"(sbase)
                : "memory", "m0");
 #else
   __builtin_amdgcn_global_load_lds(base + voff, (lds_void*)lds, 16, 0, 0);
 #endif
 }
-
-// Rescale of the output accumulators: 0 = every tile (alpha is 1 unless the
-// running max moved), 1 = only in a wave-uniform branch when some lane's max
-// moved by more than kRescaleLog2.
-#ifndef HFA_RESCALE_MODE
-#define HFA_RESCALE_MODE 1
-#endif
 
 // Wait until at most N of this wave's vector-memory operations are
 // outstanding (they complete in issue order).
@@ -215,18 +218,31 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   const int wig = wave & 3;  // wave within its group
   const __bf16* const stream_src = grp == 0 ? Kh : Vh;
   char* const stream_ring = grp == 0 ? kbuf : vbuf;
+  // Per-lane source offsets (bytes) of this lane's LD chunks within a tile:
+  // the same for every tile except a ragged last one.
+  int dma_off[T::LD];
+#pragma unroll
+  for (int u = 0; u < T::LD; ++u) {
+    const int pos = (wig * T::LD + u) * 64 + lane;  // 16-byte chunk position within the tile
+    const int row = pos / T::CH, phys = pos % T::CH;
+    const int ch = phys ^ (grp == 0 ? k_swz<T::CH>(row) : v_swz<T::CH>(row));
+    dma_off[u] = (row * D + ch * 8) * 2;
+  }
   auto issue_tile = [&](int t) {
     if (t >= ntiles) return;
     char* dst = stream_ring + (t % T::NBUF) * TILEB;
     const char* tile_src = reinterpret_cast<const char*>(stream_src + static_cast<size_t>(t) * KT * D);
-    const bool full = (t + 1) * KT <= N;  // uniform: only the last tile can be ragged
+    if ((t + 1) * KT <= N) {
 #pragma unroll
-    for (int u = 0; u < T::LD; ++u) {
-      const int pos = (wig * T::LD + u) * 64 + lane;  // 16-byte chunk position within the tile
-      const int row = pos / T::CH, phys = pos % T::CH;
-      const int ch = phys ^ (grp == 0 ? k_swz<T::CH>(row) : v_swz<T::CH>(row));
-      const int src_row = full ? row : min(row, N - 1 - t * KT);
-      dma16(tile_src, (src_row * D + ch * 8) * 2, dst + (wig * T::LD + u) * 1024);
+      for (int u = 0; u < T::LD; ++u) dma16(tile_src, dma_off[u], dst + (wig * T::LD + u) * 1024);
+    } else {  // ragged last tile: rows past the end re-read the last row
+      const int last = N - 1 - t * KT;
+#pragma unroll
+      for (int u = 0; u < T::LD; ++u) {
+        const int row = ((wig * T::LD + u) * 64 + lane) / T::CH;
+        const int off = dma_off[u] - (row > last ? (row - last) * D * 2 : 0);
+        dma16(tile_src, off, dst + (wig * T::LD + u) * 1024);
+      }
     }
   };
 
@@ -251,18 +267,14 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
     const int n = i % (D / 32), c = i / (D / 32);
     return (16 * c + vrow) * ROWB + (((4 * n + vch) ^ vswz) << 4) + vin;
   };
-  auto mfma_phase = [&](int j, auto with_pv_tag) {
+  // Operand registers of the first PF steps persist across the barrier, so
+  // that the VALU phase before an MFMA phase can already request them.
+  u32x4 kq[PF + 1];
+  s16x4 vlo[PF + 1], vhi[PF + 1];
+  auto prefetch_operands = [&](int j, auto with_pv_tag) {  // first PF steps of MFMA phase j
     constexpr bool with_pv = decltype(with_pv_tag)::value;
     const char* kt = kbuf + (j % T::NBUF) * TILEB;
     const char* vt = vbuf + ((j + T::NBUF - 1) % T::NBUF) * TILEB;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < KT / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.0f;
-    u32x4 kq[PF + 1];
-    s16x4 vlo[PF + 1], vhi[PF + 1];
 #pragma unroll
     for (int i = 0; i < PF; ++i) {
       kq[i] = lds_load16(kt, k_off(i));
@@ -271,6 +283,19 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
         vhi[i] = lds_read_tr16(vt, v_off(i) + 4 * ROWB);
       }
     }
+  };
+  auto mfma_phase = [&](int j, auto with_pv_tag, auto prefetched_tag) {
+    constexpr bool with_pv = decltype(with_pv_tag)::value;
+    constexpr bool prefetched = decltype(prefetched_tag)::value;
+    const char* kt = kbuf + (j % T::NBUF) * TILEB;
+    const char* vt = vbuf + ((j + T::NBUF - 1) % T::NBUF) * TILEB;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < KT / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.0f;
+    if (!prefetched) prefetch_operands(j, with_pv_tag);
 #pragma unroll
     for (int i = 0; i < STEPS; ++i) {
       if (i + PF < STEPS) {
@@ -295,10 +320,9 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
       }
     }
 #if HFA_SCHED_GROUPS
-    // Pin the order: the HBM prefetch loads first, then per step the operand
-    // reads of a later step followed by that step's matrix-core instructions.
-    __builtin_amdgcn_sched_group_barrier(0x020, T::LD, 0);  // VMEM reads
-    __builtin_amdgcn_sched_group_barrier(0x100, PF * (with_pv ? 3 : 1), 0);  // DS reads
+    // Pin the order: per step the operand reads of a later step, then that
+    // step's matrix-core instructions.
+    if (!prefetched) __builtin_amdgcn_sched_group_barrier(0x100, PF * (with_pv ? 3 : 1), 0);  // DS reads
 #pragma unroll
     for (int i = 0; i < STEPS; ++i) {
       if (i + PF < STEPS) __builtin_amdgcn_sched_group_barrier(0x100, with_pv ? 3 : 1, 0);
@@ -342,25 +366,21 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
+      // The lane's KT/2 scores of this tile, flattened; reductions run as
+      // balanced trees so the vector pipe is not held up by one serial chain.
+      constexpr int NS = KT / 2;
+      auto sv = [&](int i) { return s[qb][i / 16][i % 16]; };
+      float part[NS / 4];
 #pragma unroll
-      for (int kb = 0; kb < KT / 32; ++kb)
+      for (int u = 0; u < NS / 4; ++u)
+        part[u] = fmaxf(fmaxf(sv(4 * u), sv(4 * u + 1)), fmaxf(sv(4 * u + 2), sv(4 * u + 3)));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[qb][kb][r]);
-      mx = max_xor32(mx);
+      for (int w = NS / 8; w >= 1; w /= 2)
+#pragma unroll
+        for (int u = 0; u < w; ++u) part[u] = fmaxf(part[u], part[u + w]);
+      const float mx = max_xor32(part[0]);
       const float m_cand = fmaxf(m_run[qb], mx);
       const bool grow = (m_cand - m_run[qb]) * c2 > kRescaleLog2;  // always true on the first tile
-#if HFA_RESCALE_MODE == 0
-      // unconditional: straight-line code, alpha == 1 unless the max moved
-      {
-        const float m_new = grow ? m_cand : m_run[qb];
-        const float alpha = exp2_hw((m_run[qb] - m_new) * c2);  // 0 on the first tile, 1 if kept
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int n = 0; n < D / 32; ++n) acc[qb][n] *= alpha;
-        m_run[qb] = m_new;
-      }
-#else
       if (__any(grow)) {
         const float m_new = grow ? m_cand : m_run[qb];
         const float alpha = exp2_hw((m_run[qb] - m_new) * c2);  // 0 on the first tile, 1 if kept
@@ -369,18 +389,21 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
         for (int n = 0; n < D / 32; ++n) acc[qb][n] *= alpha;
         m_run[qb] = m_new;
       }
-#endif
       const float mc = m_run[qb] * c2;
-      float ts = 0.0f;
+      float pv[NS];
+#pragma unroll
+      for (int i = 0; i < NS; ++i) pv[i] = exp2_hw(fmaf(sv(i), c2, -mc));
 #pragma unroll
       for (int c = 0; c < KT / 16; ++c)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float p = exp2_hw(fmaf(s[qb][c >> 1][8 * (c & 1) + e], c2, -mc));
-          ts += p;
-          pf[qb][c][e] = static_cast<__bf16>(p);
-        }
-      l_run[qb] += ts;
+        for (int e = 0; e < 8; ++e) pf[qb][c][e] = static_cast<__bf16>(pv[8 * c + e]);
+#pragma unroll
+      for (int u = 0; u < NS / 4; ++u) part[u] = (pv[4 * u] + pv[4 * u + 1]) + (pv[4 * u + 2] + pv[4 * u + 3]);
+#pragma unroll
+      for (int w = NS / 8; w >= 1; w /= 2)
+#pragma unroll
+        for (int u = 0; u < w; ++u) part[u] += part[u + w];
+      l_run[qb] += part[0];
     }
   };
 
@@ -389,7 +412,6 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   // still be in flight is LD times the number of tiles requested after t.
   auto wait_tile = [&](int t, int newest) {
     const int after = min(newest, ntiles - 1) - t;
-    static_assert(T::AHEAD == 2, "wait_tile covers up to two newer tiles");
     if (after <= 0)
       vmcnt_wait<0>();
     else if (after == 1)
@@ -398,31 +420,41 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
       vmcnt_wait<2 * T::LD>();
   };
 
-  // ---- prologue: the first AHEAD tiles of each stream; K_0 must be in LDS
-  // before group 0's first MFMA phase.
+  // ---- prologue: the first AHEAD tiles of each stream.  K_0 and K_1 (group
+  // 0) and V_0 (group 1) must be complete before the first barrier.
 #pragma unroll
   for (int t = 0; t < T::AHEAD; ++t) issue_tile(t);
-  if (grp == 0) wait_tile(0, T::AHEAD - 1);
+  if (grp == 0)
+    wait_tile(1, T::AHEAD - 1);
+  else
+    wait_tile(0, T::AHEAD - 1);
   lds_barrier();
   if (grp == 1) lds_barrier();  // group 1 runs half a tile behind
 
-  // One tile: MFMA phase (request tile j + AHEAD of this group's stream,
-  // scores of tile j, P V of tile j - 1), then VALU phase (softmax of tile j).
-  // Tile 0 is peeled off so that the accumulator flows straight through the
-  // loop body (no path around the output MFMAs).
-  auto tile_step = [&](int j, auto with_pv_tag) {
+  // One tile: the MFMA phase (scores of tile j, P V of tile j - 1), then
+  // the VALU phase: the LDS operands of the next MFMA phase, the HBM request
+  // for tile j + AHEAD of this group's stream, the softmax of tile j, and the
+  // wait that completes the tile the other group reads first in the next
+  // VALU phase (group 0: K_{j+2}, group 1: V_{j+1}).  Tile 0 is peeled off so
+  // that the accumulator flows straight through the loop body.
+  auto valu_phase = [&](int j) {
+    if (j + 1 < ntiles) prefetch_operands(j + 1, std::true_type{});
     issue_tile(j + T::AHEAD);
-    mfma_phase(j, with_pv_tag);
-    // V_j is first read in the next interval (group 0's MFMA phase j + 1).
-    if (grp == 1) wait_tile(j, j + T::AHEAD);
-    lds_barrier();
     softmax(j);
-    // K_{j+1} is first read in the next interval (group 0's MFMA phase j + 1).
-    if (grp == 0) wait_tile(j + 1, j + T::AHEAD);
+    if (grp == 0)
+      wait_tile(j + 2, j + T::AHEAD);
+    else
+      wait_tile(j + 1, j + T::AHEAD);
     lds_barrier();
   };
-  tile_step(0, std::false_type{});
-  for (int j = 1; j < ntiles; ++j) tile_step(j, std::true_type{});
+  mfma_phase(0, std::false_type{}, std::false_type{});
+  lds_barrier();
+  valu_phase(0);
+  for (int j = 1; j < ntiles; ++j) {
+    mfma_phase(j, std::true_type{}, std::true_type{});
+    lds_barrier();
+    valu_phase(j);
+  }
   mfma_pv_only(ntiles - 1);
   if (grp == 0) lds_barrier();  // both groups execute the same number of barriers
 

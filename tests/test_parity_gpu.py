@@ -209,3 +209,46 @@ def test_status_on_device():
     with pytest.raises(hfa.HfaError) as ei:
         hfa.attn_fwd(q, q, q)
     assert ei.value.status == hfa.HFA_ERR_UNSUPPORTED
+
+
+def _views_with_high_low_word(shapes, dtype, dev):
+    """Tensors placed at device addresses whose low 32-bit word has bit 31 set.
+
+    The kernels split 64-bit source addresses into 32-bit halves; this pins
+    that the low half is widened without sign extension.
+    """
+    elt = torch.empty((), dtype=dtype).element_size()
+    sizes = [math.prod(s) * elt for s in shapes]
+    pool = torch.empty(4 * 2**30 + sum(sizes) + 4096 * len(shapes), dtype=torch.uint8, device=dev)
+    base = pool.data_ptr()
+    # first 256-byte aligned address >= base whose bit 31 is set
+    cand = (base | 0x80000000) if (base & 0x80000000) == 0 else base
+    cand = (cand + 255) & ~255
+    if cand < base:
+        cand += 2**32
+    off = cand - base
+    views = []
+    for s, nbytes in zip(shapes, sizes):
+        assert ((base + off) & 0x80000000) != 0
+        views.append(pool[off:off + nbytes].view(dtype).view(s))
+        off += (nbytes + 4095) // 4096 * 4096
+    return pool, views
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [1, 300])
+def test_addresses_with_bit31_set(dtype, d, N):
+    B, H = 1, 2
+    q, k, v = W.make_inputs(B, H, N, d, dtype, seed=31 + N + d)
+    dev = torch.device("cuda:0")
+    td = W.torch_dtype(dtype)
+    pool, (qd, kd, vd, od) = _views_with_high_low_word([(B, H, N, d)] * 4, td, dev)
+    pool2, (ld,) = _views_with_high_low_word([(B, H, N)], torch.float32, dev)
+    qd.copy_(q.to(dev)); kd.copy_(k.to(dev)); vd.copy_(v.to(dev))
+    hfa.attn_fwd(qd, kd, vd, 1.0 / math.sqrt(d), out=od, lse=ld)
+    torch.cuda.synchronize()
+    ro, rl = run_oracle(q, k, v, 1.0 / math.sqrt(d))
+    assert_close(f"bit31 {dtype} N={N} d={d}", od.float().cpu().double().numpy(), ld.cpu().double().numpy(),
+                 ro, rl, dtype)
+    del pool, pool2
