@@ -2,7 +2,7 @@
 // log-sum-exp, computed tile by tile with the online normalisation identity
 // (neuralmasteryai "Hardware Acceleration & Custom Kernels", section 2,
 // steps 1-2): each wave owns 32 query rows held in registers, K/V tiles
-// stream through double-buffered LDS, and the running max, running
+// stream through rings of LDS buffers, and the running max, running
 // denominator and running output sums are rescaled as key tiles arrive, so
 // no score ever reaches HBM.
 //
@@ -93,9 +93,20 @@ __device__ __forceinline__ int v_swz(int row) {
 #ifndef HFA_PF
 #define HFA_PF 2
 #endif
+#ifndef HFA_LAZY_MAX
+#define HFA_LAZY_MAX 1
+#endif
+#ifndef HFA_PIN_SOFTMAX
+#define HFA_PIN_SOFTMAX 1
+#endif
+#ifndef HFA_SCORES_FIRST
+#define HFA_SCORES_FIRST 1
+#endif
 
 // Largest growth of the running max (log2 units) absorbed without rescaling.
 constexpr float kRescaleLog2 = 8.0f;
+// Largest lane sum of one tile's weights accepted without forming the max.
+constexpr float kSumLimit = 65536.0f;
 
 // Workgroup barrier that waits only for this wave's LDS operations: global
 // loads issued before it stay in flight.  The memory clobber keeps the
@@ -124,8 +135,14 @@ __device__ __forceinline__ void dma16(const char* base, int voff, char* lds) {
   const uint32_t b_lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b))));
   const uint32_t b_hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b >> 32))));
   const uint64_t sbase = (static_cast<uint64_t>(b_hi) << 32) | static_cast<uint64_t>(b_lo);
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds_addr), "v"(voff), "s"(sbase)
-               : "memory", "m0");
+  // M0 carries the LDS destination; its previous value is restored, so the
+  // statement leaves every register the compiler may rely on unchanged.
+  uint32_t saved_m0;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved_m0)
+      : "s"(lds_addr), "v"(voff), "s"(sbase)
+      : "memory");
 #else
   __builtin_amdgcn_global_load_lds(base + voff, (lds_void*)lds, 16, 0, 0);
 #endif
@@ -267,26 +284,40 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
     const int n = i % (D / 32), c = i / (D / 32);
     return (16 * c + vrow) * ROWB + (((4 * n + vch) ^ vswz) << 4) + vin;
   };
-  // Operand registers of the first PF steps persist across the barrier, so
-  // that the VALU phase before an MFMA phase can already request them.
-  u32x4 kq[PF + 1];
-  s16x4 vlo[PF + 1], vhi[PF + 1];
-  auto prefetch_operands = [&](int j, auto with_pv_tag) {  // first PF steps of MFMA phase j
+  // The MFMA phase is a sequence of operations, each one MFMA with its LDS
+  // operand: with HFA_SCORES_FIRST the SSTEPS score MFMAs come first (so the
+  // scores are complete, and the softmax can start, while the output MFMAs
+  // still run), otherwise score and output MFMAs alternate.  Operands are
+  // requested PF operations ahead; the first PF of them persist across the
+  // barrier, so that the VALU phase before can already request them.
+  constexpr int NOPS = SSTEPS + VSTEPS;
+  auto op_is_score = [&](int i, bool with_pv) {
+    if (!with_pv) return true;
+    return HFA_SCORES_FIRST ? (i < SSTEPS) : (i % 2 == 0);
+  };
+  auto op_step = [&](int i, bool with_pv) {  // index of the score or output step of operation i
+    if (!with_pv) return i;
+    return HFA_SCORES_FIRST ? (i < SSTEPS ? i : i - SSTEPS) : i / 2;
+  };
+  u32x4 opnd[PF + 1];
+  auto load_op = [&](int i, bool with_pv, const char* kt, const char* vt) -> u32x4 {
+    const int st = op_step(i, with_pv);
+    if (op_is_score(i, with_pv)) return lds_load16(kt, k_off(st));
+    const s16x4 lo = lds_read_tr16(vt, v_off(st));
+    const s16x4 hi = lds_read_tr16(vt, v_off(st) + 4 * ROWB);
+    return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto prefetch_operands = [&](int j, auto with_pv_tag) {  // first PF operations of MFMA phase j
     constexpr bool with_pv = decltype(with_pv_tag)::value;
     const char* kt = kbuf + (j % T::NBUF) * TILEB;
     const char* vt = vbuf + ((j + T::NBUF - 1) % T::NBUF) * TILEB;
 #pragma unroll
-    for (int i = 0; i < PF; ++i) {
-      kq[i] = lds_load16(kt, k_off(i));
-      if (with_pv) {
-        vlo[i] = lds_read_tr16(vt, v_off(i));
-        vhi[i] = lds_read_tr16(vt, v_off(i) + 4 * ROWB);
-      }
-    }
+    for (int i = 0; i < PF; ++i) opnd[i] = load_op(i, with_pv, kt, vt);
   };
   auto mfma_phase = [&](int j, auto with_pv_tag, auto prefetched_tag) {
     constexpr bool with_pv = decltype(with_pv_tag)::value;
     constexpr bool prefetched = decltype(prefetched_tag)::value;
+    constexpr int nops = with_pv ? NOPS : SSTEPS;
     const char* kt = kbuf + (j % T::NBUF) * TILEB;
     const char* vt = vbuf + ((j + T::NBUF - 1) % T::NBUF) * TILEB;
 #pragma unroll
@@ -297,36 +328,61 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
         for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.0f;
     if (!prefetched) prefetch_operands(j, with_pv_tag);
 #pragma unroll
-    for (int i = 0; i < STEPS; ++i) {
-      if (i + PF < STEPS) {
-        kq[(i + PF) % (PF + 1)] = lds_load16(kt, k_off(i + PF));
-        if (with_pv) {
-          vlo[(i + PF) % (PF + 1)] = lds_read_tr16(vt, v_off(i + PF));
-          vhi[(i + PF) % (PF + 1)] = lds_read_tr16(vt, v_off(i + PF) + 4 * ROWB);
-        }
-      }
-      const int kb = i % (KT / 32), t = i / (KT / 32);
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kq[i % (PF + 1)]),
-                                                            __builtin_bit_cast(bf16x8, qf[qb][t]), s[qb][kb], 0, 0, 0);
-      if (with_pv) {
-        const int n = i % (D / 32), c = i / (D / 32);
-        const bf16x8 vf = __builtin_bit_cast(
-            bf16x8, __builtin_shufflevector(vlo[i % (PF + 1)], vhi[i % (PF + 1)], 0, 1, 2, 3, 4, 5, 6, 7));
+    for (int i = 0; i < nops; ++i) {
+      if (i + PF < nops) opnd[(i + PF) % (PF + 1)] = load_op(i + PF, with_pv, kt, vt);
+      const int st = op_step(i, with_pv);
+      const u32x4 a = opnd[i % (PF + 1)];
+      if (op_is_score(i, with_pv)) {
+        const int kb = st % (KT / 32), t = st / (KT / 32);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          acc[qb][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][c], acc[qb][n], 0, 0, 0);
+          s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                              __builtin_bit_cast(bf16x8, qf[qb][t]), s[qb][kb], 0, 0, 0);
+      } else {
+        const int n = st % (D / 32), c = st / (D / 32);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          acc[qb][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pf[qb][c], acc[qb][n],
+                                                               0, 0, 0);
       }
     }
 #if HFA_SCHED_GROUPS
-    // Pin the order: per step the operand reads of a later step, then that
-    // step's matrix-core instructions.
-    if (!prefetched) __builtin_amdgcn_sched_group_barrier(0x100, PF * (with_pv ? 3 : 1), 0);  // DS reads
+    // Pin the order: per operation the operand reads of a later one (1 read
+    // for a score operand, 2 transposing reads for an output operand), then
+    // this operation's MFMA.
+    if constexpr (!with_pv) {
+      if (!prefetched) __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);
 #pragma unroll
-    for (int i = 0; i < STEPS; ++i) {
-      if (i + PF < STEPS) __builtin_amdgcn_sched_group_barrier(0x100, with_pv ? 3 : 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, (with_pv ? 2 : 1) * QB, 0);  // MFMA
+      for (int i = 0; i < nops; ++i) {
+        if (i + PF < nops) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      }
+    } else if constexpr (HFA_SCORES_FIRST) {
+      if (!prefetched) __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);  // PF <= SSTEPS score operands
+#pragma unroll
+      for (int i = 0; i < SSTEPS - PF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      }
+#pragma unroll
+      for (int i = SSTEPS - PF; i < nops - PF; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      }
+#pragma unroll
+      for (int i = nops - PF; i < nops; ++i) __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+    } else {
+      static_assert(PF % 2 == 0, "alternating order pins reads in (score, output) pairs");
+      if (!prefetched) __builtin_amdgcn_sched_group_barrier(0x100, 3 * PF / 2, 0);
+#pragma unroll
+      for (int i = 0; i < nops - PF; i += 2) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+      }
+#pragma unroll
+      for (int i = nops - PF; i < nops; ++i) __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
     }
 #endif
   };
@@ -351,7 +407,16 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   // p <= 2^kRescaleLog2, which the fp32 sums and the bf16 P represent with
   // unchanged relative precision, and the final division by the denominator
   // removes it exactly.  The rescale is then a rare, wave-uniform branch.
-  auto softmax = [&](int j) {
+  //
+  // With HFA_LAZY_MAX, tiles after the first do not even form the row max
+  // up front: they exponentiate against the running max straight away and
+  // check afterwards, on the lane's sum of the tile's weights, whether some
+  // weight outgrew the bound (a sum above kSumLimit implies a weight above
+  // kSumLimit / (KT/2) = 2^11, that is a growth beyond kRescaleLog2, so the
+  // recomputation below then does rescale).  Only then is the tile redone
+  // with its max.  Every weight stays <= kSumLimit either way.
+  auto softmax = [&](int j, auto first_tag) {
+    constexpr bool first = decltype(first_tag)::value;
     const int key0 = j * KT;
     if (key0 + KT > N) {  // keys past the end of the sequence get score -inf (weight 0)
 #pragma unroll
@@ -370,40 +435,63 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
       // balanced trees so the vector pipe is not held up by one serial chain.
       constexpr int NS = KT / 2;
       auto sv = [&](int i) { return s[qb][i / 16][i % 16]; };
-      float part[NS / 4];
-#pragma unroll
-      for (int u = 0; u < NS / 4; ++u)
-        part[u] = fmaxf(fmaxf(sv(4 * u), sv(4 * u + 1)), fmaxf(sv(4 * u + 2), sv(4 * u + 3)));
-#pragma unroll
-      for (int w = NS / 8; w >= 1; w /= 2)
-#pragma unroll
-        for (int u = 0; u < w; ++u) part[u] = fmaxf(part[u], part[u + w]);
-      const float mx = max_xor32(part[0]);
-      const float m_cand = fmaxf(m_run[qb], mx);
-      const bool grow = (m_cand - m_run[qb]) * c2 > kRescaleLog2;  // always true on the first tile
-      if (__any(grow)) {
-        const float m_new = grow ? m_cand : m_run[qb];
-        const float alpha = exp2_hw((m_run[qb] - m_new) * c2);  // 0 on the first tile, 1 if kept
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int n = 0; n < D / 32; ++n) acc[qb][n] *= alpha;
-        m_run[qb] = m_new;
-      }
-      const float mc = m_run[qb] * c2;
       float pv[NS];
+      auto exp_and_sum = [&]() {  // weights against the running max, and their lane sum
+        const float mc = m_run[qb] * c2;
 #pragma unroll
-      for (int i = 0; i < NS; ++i) pv[i] = exp2_hw(fmaf(sv(i), c2, -mc));
+        for (int i = 0; i < NS; ++i) pv[i] = exp2_hw(fmaf(sv(i), c2, -mc));
+        float part[NS / 4];
+#pragma unroll
+        for (int u = 0; u < NS / 4; ++u) part[u] = (pv[4 * u] + pv[4 * u + 1]) + (pv[4 * u + 2] + pv[4 * u + 3]);
+#pragma unroll
+        for (int w = NS / 8; w >= 1; w /= 2)
+#pragma unroll
+          for (int u = 0; u < w; ++u) part[u] += part[u + w];
+        return part[0];
+      };
+      auto with_max = [&]() {  // row max, rescale if it grew too far, then the weights
+        float part[NS / 4];
+#pragma unroll
+        for (int u = 0; u < NS / 4; ++u)
+          part[u] = fmaxf(fmaxf(sv(4 * u), sv(4 * u + 1)), fmaxf(sv(4 * u + 2), sv(4 * u + 3)));
+#pragma unroll
+        for (int w = NS / 8; w >= 1; w /= 2)
+#pragma unroll
+          for (int u = 0; u < w; ++u) part[u] = fmaxf(part[u], part[u + w]);
+        const float mx = max_xor32(part[0]);
+        const float m_cand = fmaxf(m_run[qb], mx);
+        const bool grow = (m_cand - m_run[qb]) * c2 > kRescaleLog2;  // always true on the first tile
+        if (__any(grow)) {
+          const float m_new = grow ? m_cand : m_run[qb];
+          const float alpha = exp2_hw((m_run[qb] - m_new) * c2);  // 0 on the first tile, 1 if kept
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int n = 0; n < D / 32; ++n) acc[qb][n] *= alpha;
+          m_run[qb] = m_new;
+        }
+        return exp_and_sum();
+      };
+      float tsum;
+      if constexpr (first || !HFA_LAZY_MAX) {
+        tsum = with_max();
+      } else {
+        // m_run is finite here (tile 0 holds key 0), so no weight is NaN.
+        tsum = exp_and_sum();
+        if (__any(!(tsum <= kSumLimit))) tsum = with_max();
+      }
 #pragma unroll
       for (int c = 0; c < KT / 16; ++c)
 #pragma unroll
         for (int e = 0; e < 8; ++e) pf[qb][c][e] = static_cast<__bf16>(pv[8 * c + e]);
+      l_run[qb] += tsum;
+#if HFA_PIN_SOFTMAX
+      // An empty statement that consumes P and the denominator: the compiler
+      // would otherwise sink the exponentials below the wait for the next
+      // K/V tile that follows, exposing HBM latency in this phase.
 #pragma unroll
-      for (int u = 0; u < NS / 4; ++u) part[u] = (pv[4 * u] + pv[4 * u + 1]) + (pv[4 * u + 2] + pv[4 * u + 3]);
-#pragma unroll
-      for (int w = NS / 8; w >= 1; w /= 2)
-#pragma unroll
-        for (int u = 0; u < w; ++u) part[u] += part[u + w];
-      l_run[qb] += part[0];
+      for (int c = 0; c < KT / 16; ++c) asm volatile("" ::"v"(__builtin_bit_cast(u32x4, pf[qb][c])));
+      asm volatile("" ::"v"(l_run[qb]));
+#endif
     }
   };
 
@@ -437,10 +525,10 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   // wait that completes the tile the other group reads first in the next
   // VALU phase (group 0: K_{j+2}, group 1: V_{j+1}).  Tile 0 is peeled off so
   // that the accumulator flows straight through the loop body.
-  auto valu_phase = [&](int j) {
+  auto valu_phase = [&](int j, auto first_tag) {
     if (j + 1 < ntiles) prefetch_operands(j + 1, std::true_type{});
     issue_tile(j + T::AHEAD);
-    softmax(j);
+    softmax(j, first_tag);
     if (grp == 0)
       wait_tile(j + 2, j + T::AHEAD);
     else
@@ -449,11 +537,11 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   };
   mfma_phase(0, std::false_type{}, std::false_type{});
   lds_barrier();
-  valu_phase(0);
+  valu_phase(0, std::true_type{});
   for (int j = 1; j < ntiles; ++j) {
     mfma_phase(j, std::true_type{}, std::true_type{});
     lds_barrier();
-    valu_phase(j);
+    valu_phase(j, std::false_type{});
   }
   mfma_pv_only(ntiles - 1);
   if (grp == 0) lds_barrier();  // both groups execute the same number of barriers

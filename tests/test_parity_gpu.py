@@ -40,7 +40,10 @@ def run_gpu(q, k, v, scale):
 
 
 def run_oracle(q, k, v, scale, rows=None):
-    return oracle.attn_fwd(*(W.to_oracle_array(t) for t in (q, k, v)), scale, rows=rows)
+    # The C ABI takes the scale as fp32: the oracle gets that same value, so
+    # both sides compute the same function (1/sqrt(128) moves by 1.7e-8
+    # relative when rounded, 3.6e-6 on a log-sum-exp of 200).
+    return oracle.attn_fwd(*(W.to_oracle_array(t) for t in (q, k, v)), float(np.float32(scale)), rows=rows)
 
 
 def f32_tolerance(ref):
@@ -121,6 +124,26 @@ def test_peaked_rows(dtype):
     # Q and K x8: score standard deviation ~ 64 * scale; stresses the rescale.
     q, k, v = W.make_inputs(2, 2, 700, 64, dtype, seed=77, qk_mult=8.0)
     check_case(f"peaked {dtype}", q, k, v, 0.125, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_rising_scores(dtype, d):
+    # Scores drift linearly along the keys, with a slope that differs per
+    # query row (some rows fall, most rise by up to ~15 log2 units per
+    # 64-key tile): the running max moves on most tiles, by amounts on both sides of
+    # every rescale threshold.
+    N = 1000
+    g = torch.Generator("cpu").manual_seed(900 + d)
+    e = torch.ones(d) / math.sqrt(d)
+    slope = torch.linspace(-0.2, 1.0, N).view(N, 1)          # per query row
+    ramp = torch.linspace(0.0, 1.0, N).view(N, 1)            # per key
+    q = torch.randn(1, 2, N, d, generator=g) + 8.0 * slope * e
+    k = torch.randn(1, 2, N, d, generator=g) + 20.75 * math.sqrt(d) * ramp * e
+    v = torch.randn(1, 2, N, d, generator=g)
+    td = W.torch_dtype(dtype)
+    q, k, v = (t.to(td).contiguous() for t in (q, k, v))
+    check_case(f"rising {dtype} d={d}", q, k, v, 1.0 / math.sqrt(d), dtype)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
