@@ -25,6 +25,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -44,12 +45,17 @@ def log(msg: str) -> None:
 
 
 def kernel_source_digest() -> str:
-    """Digest of the HIP sources: counter figures are only valid for the kernel they were taken on."""
+    """Digest of the HIP sources: counter figures are only valid for the kernel they were taken on.
+
+    Line comments and whitespace are dropped first, so editing prose does not void figures
+    taken on the same code."""
     h = hashlib.sha256()
     for path in sorted(glob.glob(os.path.join(ROOT, "fa2_fwd_amd", "csrc", "*"))):
-        with open(path, "rb") as f:
-            h.update(os.path.basename(path).encode())
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            text = f.read()
+        code = "".join(re.sub(r"//.*", "", line).strip() for line in text.splitlines())
+        h.update(os.path.basename(path).encode())
+        h.update(re.sub(r"\s+", "", code).encode())
     return h.hexdigest()[:16]
 
 
