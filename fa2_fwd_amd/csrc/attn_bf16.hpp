@@ -32,13 +32,14 @@
 // barrier later, in every interval one wave of each SIMD issues matrix-core
 // work while the other runs its softmax on the vector unit.
 //
-// LDS tiles: K_t and V_t live in buffer t % 4 of two rings filled straight
-// from HBM.  In its VALU phase j, group 0 requests K_{j+3} and group 1
-// requests V_{j+3}; each waits for its own earlier requests (K_{j+2},
-// respectively V_{j+1}) just before the barrier, so that in the next VALU
-// phase both groups can already read the operands of their next MFMA phase.
-// Across the barrier intervals a buffer is refilled only after both groups
-// finished reading its previous tile.
+// LDS tiles: K_t and V_t live in buffer t % NBUF of two rings filled
+// straight from HBM.  In its VALU phase j, group 0 requests K_{j+3} and
+// group 1 requests V_{j+3}; at the end of its next MFMA phase each waits for
+// the tile that is read first after the following barrier (group 0: K_{j+1}
+// at the end of MFMA phase j, read ahead by both groups' VALU phases;
+// group 1: V_j, read by group 0's next MFMA phase).  Across the barrier
+// intervals a buffer is refilled only after both groups finished reading its
+// previous tile (tests/test_schedule_model.py checks both properties).
 #pragma once
 
 #include <type_traits>
@@ -46,6 +47,13 @@
 #include "common.hpp"
 
 namespace hfa {
+
+#ifndef HFA_NBUF
+#define HFA_NBUF 4
+#endif
+#ifndef HFA_DOT2_SUM
+#define HFA_DOT2_SUM 0
+#endif
 
 template <int D_, int QB_, int NW_>
 struct Bf16Tile {
@@ -59,8 +67,8 @@ struct Bf16Tile {
   static constexpr int ROWB = D * 2;  // bytes per K or V row in LDS (XOR-swizzled, unpadded)
   static constexpr int TILEB = KT * ROWB;
   static constexpr int CH = D / 8;             // 16-byte chunks per row
-  static constexpr int NBUF = 4;               // LDS ring depth, tiles per tensor
-  static constexpr int AHEAD = 3;              // tiles of each stream requested ahead
+  static constexpr int NBUF = HFA_NBUF;        // LDS ring depth, tiles per tensor
+  static constexpr int AHEAD = NBUF - 1;       // tiles of each stream requested ahead
   static constexpr int LD = TILEB / (4 * 64 * 16);  // 16-byte loads per lane per tile (one group of 4 waves)
   static constexpr int LDS_BYTES = 2 * NBUF * TILEB;  // K ring and V ring
   static_assert(LD >= 1 && TILEB % (4 * 64 * 16) == 0, "a tile must split into whole load instructions");
@@ -99,14 +107,28 @@ __device__ __forceinline__ int v_swz(int row) {
 #ifndef HFA_PIN_SOFTMAX
 #define HFA_PIN_SOFTMAX 1
 #endif
-#ifndef HFA_SCORES_FIRST
-#define HFA_SCORES_FIRST 1
-#endif
 
 // Largest growth of the running max (log2 units) absorbed without rescaling.
 constexpr float kRescaleLog2 = 8.0f;
 // Largest lane sum of one tile's weights accepted without forming the max.
 constexpr float kSumLimit = 65536.0f;
+
+#ifndef HFA_MFMA_PRIO
+#define HFA_MFMA_PRIO 1
+#endif
+
+// Wave issue priority (s_setprio).  The SIMD arbiter otherwise favours the
+// older of its two waves, so the softmax of group 0 would take issue slots
+// from the MFMA phase of group 1; the wave in its MFMA phase runs at the
+// raised priority instead, and the matrix core is fed first.
+__device__ __forceinline__ void wave_prio(bool mfma_phase) {
+  __builtin_amdgcn_sched_barrier(0);
+  if (mfma_phase)
+    __builtin_amdgcn_s_setprio(HFA_MFMA_PRIO);
+  else
+    __builtin_amdgcn_s_setprio(0);
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 // Workgroup barrier that waits only for this wave's LDS operations: global
 // loads issued before it stay in flight.  The memory clobber keeps the
@@ -212,10 +234,10 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   const int vin = (l16 & 1) * 8;
 
   f32x16 acc[QB][D / 32];
-  float m_run[QB], l_run[QB];
+  float m2[QB], l_run[QB];  // running max (log2 units: max score * c2) and denominator
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
+    m2[qb] = -INFINITY;
     l_run[qb] = 0.0f;
 #pragma unroll
     for (int n = 0; n < D / 32; ++n)
@@ -285,20 +307,18 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
     return (16 * c + vrow) * ROWB + (((4 * n + vch) ^ vswz) << 4) + vin;
   };
   // The MFMA phase is a sequence of operations, each one MFMA with its LDS
-  // operand: with HFA_SCORES_FIRST the SSTEPS score MFMAs come first (so the
-  // scores are complete, and the softmax can start, while the output MFMAs
-  // still run), otherwise score and output MFMAs alternate.  Operands are
-  // requested PF operations ahead; the first PF of them persist across the
-  // barrier, so that the VALU phase before can already request them.
+  // operand: the SSTEPS score MFMAs first (so the scores are complete, and
+  // the softmax can start, while the output MFMAs still run), then the
+  // output MFMAs.  Operands are requested PF operations ahead; the first PF
+  // of them are read in the VALU phase before, across the barrier.
   constexpr int NOPS = SSTEPS + VSTEPS;
-  auto op_is_score = [&](int i, bool with_pv) {
-    if (!with_pv) return true;
-    return HFA_SCORES_FIRST ? (i < SSTEPS) : (i % 2 == 0);
-  };
+  auto op_is_score = [&](int i, bool with_pv) { return !with_pv || i < SSTEPS; };
   auto op_step = [&](int i, bool with_pv) {  // index of the score or output step of operation i
-    if (!with_pv) return i;
-    return HFA_SCORES_FIRST ? (i < SSTEPS ? i : i - SSTEPS) : i / 2;
+    return (!with_pv || i < SSTEPS) ? i : i - SSTEPS;
   };
+  // The operands read before the barrier (the first PF operations) are K
+  // operands only: V tiles are published one interval later (see the waits).
+  static_assert(PF <= SSTEPS, "only score operands are read ahead of the MFMA phase");
   u32x4 opnd[PF + 1];
   auto load_op = [&](int i, bool with_pv, const char* kt, const char* vt) -> u32x4 {
     const int st = op_step(i, with_pv);
@@ -357,7 +377,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
         if (i + PF < nops) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
       }
-    } else if constexpr (HFA_SCORES_FIRST) {
+    } else {
       if (!prefetched) __builtin_amdgcn_sched_group_barrier(0x100, PF, 0);  // PF <= SSTEPS score operands
 #pragma unroll
       for (int i = 0; i < SSTEPS - PF; ++i) {
@@ -366,18 +386,6 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
       }
 #pragma unroll
       for (int i = SSTEPS - PF; i < nops - PF; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
-      }
-#pragma unroll
-      for (int i = nops - PF; i < nops; ++i) __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
-    } else {
-      static_assert(PF % 2 == 0, "alternating order pins reads in (score, output) pairs");
-      if (!prefetched) __builtin_amdgcn_sched_group_barrier(0x100, 3 * PF / 2, 0);
-#pragma unroll
-      for (int i = 0; i < nops - PF; i += 2) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
       }
@@ -402,19 +410,18 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   };
 
   // ---- vector work of one interval: online softmax update of tile j.
-  // The running max only moves when it would grow by more than kRescaleLog2
-  // (log2 units) for some lane of the wave: a stale max keeps every
-  // p <= 2^kRescaleLog2, which the fp32 sums and the bf16 P represent with
-  // unchanged relative precision, and the final division by the denominator
-  // removes it exactly.  The rescale is then a rare, wave-uniform branch.
+  // The running max is kept in log2 units (m2 = max score * c2).  It only
+  // moves when it would grow by more than kRescaleLog2 for some lane of the
+  // wave: a stale max keeps every weight <= 2^kRescaleLog2, which the fp32
+  // sums and the bf16 P represent with unchanged relative precision, and the
+  // final division by the denominator removes it exactly.
   //
-  // With HFA_LAZY_MAX, tiles after the first do not even form the row max
-  // up front: they exponentiate against the running max straight away and
-  // check afterwards, on the lane's sum of the tile's weights, whether some
-  // weight outgrew the bound (a sum above kSumLimit implies a weight above
-  // kSumLimit / (KT/2) = 2^11, that is a growth beyond kRescaleLog2, so the
-  // recomputation below then does rescale).  Only then is the tile redone
-  // with its max.  Every weight stays <= kSumLimit either way.
+  // Only the first tile forms its row max up front.  Later tiles turn their
+  // scores in place into x = s * c2 - m2 and exponentiate straight away; a
+  // lane sum of the weights above kSumLimit implies a weight above
+  // kSumLimit / (KT/2) = 2^11, a growth beyond kRescaleLog2, and only then is
+  // the row max of x formed, the rescale applied and the weights redone (a
+  // rare, wave-uniform branch).  Every weight stays <= kSumLimit either way.
   auto softmax = [&](int j, auto first_tag) {
     constexpr bool first = decltype(first_tag)::value;
     const int key0 = j * KT;
@@ -431,15 +438,45 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
     }
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      // The lane's KT/2 scores of this tile, flattened; reductions run as
+      // The lane's KT/2 values of this tile, flattened; reductions run as
       // balanced trees so the vector pipe is not held up by one serial chain.
       constexpr int NS = KT / 2;
-      auto sv = [&](int i) { return s[qb][i / 16][i % 16]; };
-      float pv[NS];
-      auto exp_and_sum = [&]() {  // weights against the running max, and their lane sum
-        const float mc = m_run[qb] * c2;
+      auto xv = [&](int i) { return s[qb][i / 16][i % 16]; };
+      auto xset = [&](int i, float v) { s[qb][i / 16][i % 16] = v; };
+      auto row_max = [&]() {  // max over the row (this lane and the lane 32 apart)
+        float part[NS / 4];
 #pragma unroll
-        for (int i = 0; i < NS; ++i) pv[i] = exp2_hw(fmaf(sv(i), c2, -mc));
+        for (int u = 0; u < NS / 4; ++u)
+          part[u] = fmaxf(fmaxf(xv(4 * u), xv(4 * u + 1)), fmaxf(xv(4 * u + 2), xv(4 * u + 3)));
+#pragma unroll
+        for (int w = NS / 8; w >= 1; w /= 2)
+#pragma unroll
+          for (int u = 0; u < w; ++u) part[u] = fmaxf(part[u], part[u + w]);
+        return max_xor32(part[0]);
+      };
+      // weights p = 2^x rounded to bf16 into P, and their lane sum
+      auto weights = [&]() {
+        float pv[NS];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) pv[i] = exp2_hw(xv(i));
+#pragma unroll
+        for (int c = 0; c < KT / 16; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pf[qb][c][e] = static_cast<__bf16>(pv[8 * c + e]);
+#if HFA_DOT2_SUM
+        // the sum of the bf16-rounded weights (the ones that multiply V), two
+        // per v_dot2c_f32_bf16 against (1, 1), in four independent chains
+        const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+        float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c = 0; c < KT / 16; ++c)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2 pair = {pf[qb][c][2 * e], pf[qb][c][2 * e + 1]};
+            part[e] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, part[e], false);
+          }
+        return (part[0] + part[1]) + (part[2] + part[3]);
+#else
         float part[NS / 4];
 #pragma unroll
         for (int u = 0; u < NS / 4; ++u) part[u] = (pv[4 * u] + pv[4 * u + 1]) + (pv[4 * u + 2] + pv[4 * u + 3]);
@@ -448,41 +485,55 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
 #pragma unroll
           for (int u = 0; u < w; ++u) part[u] += part[u + w];
         return part[0];
-      };
-      auto with_max = [&]() {  // row max, rescale if it grew too far, then the weights
-        float part[NS / 4];
-#pragma unroll
-        for (int u = 0; u < NS / 4; ++u)
-          part[u] = fmaxf(fmaxf(sv(4 * u), sv(4 * u + 1)), fmaxf(sv(4 * u + 2), sv(4 * u + 3)));
-#pragma unroll
-        for (int w = NS / 8; w >= 1; w /= 2)
-#pragma unroll
-          for (int u = 0; u < w; ++u) part[u] = fmaxf(part[u], part[u + w]);
-        const float mx = max_xor32(part[0]);
-        const float m_cand = fmaxf(m_run[qb], mx);
-        const bool grow = (m_cand - m_run[qb]) * c2 > kRescaleLog2;  // always true on the first tile
-        if (__any(grow)) {
-          const float m_new = grow ? m_cand : m_run[qb];
-          const float alpha = exp2_hw((m_run[qb] - m_new) * c2);  // 0 on the first tile, 1 if kept
-          l_run[qb] *= alpha;
-#pragma unroll
-          for (int n = 0; n < D / 32; ++n) acc[qb][n] *= alpha;
-          m_run[qb] = m_new;
-        }
-        return exp_and_sum();
+#endif
       };
       float tsum;
       if constexpr (first || !HFA_LAZY_MAX) {
-        tsum = with_max();
+        if constexpr (first) {
+          // m2 is -inf before the first tile: start it at this tile's row max
+          // (finite, key 0 is in the tile), so every x <= 0.
+#pragma unroll
+          for (int i = 0; i < NS; ++i) xset(i, xv(i) * c2);
+          m2[qb] = row_max();
+#pragma unroll
+          for (int i = 0; i < NS; ++i) xset(i, xv(i) - m2[qb]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < NS; ++i) xset(i, fmaf(xv(i), c2, -m2[qb]));
+          const float mx = row_max();
+          const bool grow = mx > kRescaleLog2;
+          if (__any(grow)) {
+            const float m_new = grow ? m2[qb] + mx : m2[qb];
+            const float d = m_new - m2[qb];
+            const float alpha = exp2_hw(-d);
+            l_run[qb] *= alpha;
+#pragma unroll
+            for (int n = 0; n < D / 32; ++n) acc[qb][n] *= alpha;
+            m2[qb] = m_new;
+#pragma unroll
+            for (int i = 0; i < NS; ++i) xset(i, xv(i) - d);
+          }
+        }
+        tsum = weights();
       } else {
-        // m_run is finite here (tile 0 holds key 0), so no weight is NaN.
-        tsum = exp_and_sum();
-        if (__any(!(tsum <= kSumLimit))) tsum = with_max();
+#pragma unroll
+        for (int i = 0; i < NS; ++i) xset(i, fmaf(xv(i), c2, -m2[qb]));
+        tsum = weights();  // m2 is finite after the first tile: no x is NaN
+        if (__any(!(tsum <= kSumLimit))) {
+          const float mx = row_max();  // growth of the row max, log2 units
+          const bool grow = mx > kRescaleLog2;
+          const float m_new = grow ? m2[qb] + mx : m2[qb];
+          const float d = m_new - m2[qb];
+          const float alpha = exp2_hw(-d);
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int n = 0; n < D / 32; ++n) acc[qb][n] *= alpha;
+          m2[qb] = m_new;
+#pragma unroll
+          for (int i = 0; i < NS; ++i) xset(i, xv(i) - d);
+          tsum = weights();
+        }
       }
-#pragma unroll
-      for (int c = 0; c < KT / 16; ++c)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[qb][c][e] = static_cast<__bf16>(pv[8 * c + e]);
       l_run[qb] += tsum;
 #if HFA_PIN_SOFTMAX
       // An empty statement that consumes P and the denominator: the compiler
@@ -500,50 +551,62 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   // still be in flight is LD times the number of tiles requested after t.
   auto wait_tile = [&](int t, int newest) {
     const int after = min(newest, ntiles - 1) - t;
+    static_assert(T::AHEAD <= 4, "wait counts are spelled out up to three newer tiles");
     if (after <= 0)
       vmcnt_wait<0>();
     else if (after == 1)
       vmcnt_wait<T::LD>();
-    else
+    else if (after == 2 || T::AHEAD < 4)
       vmcnt_wait<2 * T::LD>();
+    else
+      vmcnt_wait<3 * T::LD>();
   };
 
-  // ---- prologue: the first AHEAD tiles of each stream.  K_0 and K_1 (group
-  // 0) and V_0 (group 1) must be complete before the first barrier.
+  // ---- prologue: the first AHEAD tiles of each stream; K_0 (group 0) must
+  // be complete before the first barrier.
 #pragma unroll
   for (int t = 0; t < T::AHEAD; ++t) issue_tile(t);
-  if (grp == 0)
-    wait_tile(1, T::AHEAD - 1);
-  else
-    wait_tile(0, T::AHEAD - 1);
+  if (grp == 0) wait_tile(0, T::AHEAD - 1);
   lds_barrier();
   if (grp == 1) lds_barrier();  // group 1 runs half a tile behind
 
-  // One tile: the MFMA phase (scores of tile j, P V of tile j - 1), then
-  // the VALU phase: the LDS operands of the next MFMA phase, the HBM request
-  // for tile j + AHEAD of this group's stream, the softmax of tile j, and the
-  // wait that completes the tile the other group reads first in the next
-  // VALU phase (group 0: K_{j+2}, group 1: V_{j+1}).  Tile 0 is peeled off so
-  // that the accumulator flows straight through the loop body.
+  // One tile: the MFMA phase (scores of tile j, P V of tile j - 1) and the
+  // wait that completes the tile read first after its closing barrier:
+  // group 0 needs K_{j+1} (operands read ahead in both groups' next VALU
+  // phases), group 1 needs V_j (read by group 0's next MFMA phase).  Each
+  // was requested AHEAD tiles earlier, three to four intervals before.
+  // Then the VALU phase: the first LDS operands of the next MFMA phase, the
+  // HBM request for tile j + AHEAD of this group's stream and the softmax of
+  // tile j.  Tile 0 is peeled off so that the accumulator flows straight
+  // through the loop body.
+  auto close_mfma_phase = [&](int j) {
+    if (grp == 0)
+      wait_tile(j + 1, j - 1 + T::AHEAD);
+    else
+      wait_tile(j, j - 1 + T::AHEAD);
+    lds_barrier();
+  };
   auto valu_phase = [&](int j, auto first_tag) {
     if (j + 1 < ntiles) prefetch_operands(j + 1, std::true_type{});
     issue_tile(j + T::AHEAD);
     softmax(j, first_tag);
-    if (grp == 0)
-      wait_tile(j + 2, j + T::AHEAD);
-    else
-      wait_tile(j + 1, j + T::AHEAD);
     lds_barrier();
   };
+  wave_prio(true);
   mfma_phase(0, std::false_type{}, std::false_type{});
-  lds_barrier();
+  wave_prio(false);
+  close_mfma_phase(0);
   valu_phase(0, std::true_type{});
   for (int j = 1; j < ntiles; ++j) {
+    wave_prio(true);
     mfma_phase(j, std::true_type{}, std::true_type{});
-    lds_barrier();
+    wave_prio(false);
+    close_mfma_phase(j);
     valu_phase(j, std::false_type{});
   }
+  wave_prio(true);
   mfma_pv_only(ntiles - 1);
+  wave_prio(false);
   if (grp == 0) lds_barrier();  // both groups execute the same number of barriers
 
   // ---- epilogue: normalise, round to bf16, one write of O and of LSE
@@ -565,7 +628,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
         }
       if (hh == 0) {
         const double lse2 =
-            static_cast<double>(m_run[qb]) * static_cast<double>(c2) + log2(static_cast<double>(l_tot));
+            static_cast<double>(m2[qb]) + log2(static_cast<double>(l_tot));
         LSE[static_cast<size_t>(bh) * N + row] = static_cast<float>(lse2 * kLn2);
       }
     }

@@ -8,17 +8,19 @@ and when its requester waits for it, and checks the two properties the
 kernel relies on:
 
 1. every LDS read of a tile happens in an interval after the one whose
-   closing barrier follows the requester's wait for that tile;
+   closing barrier follows the requester's wait for that tile (group 0 waits
+   for K_{j+1} at the end of its MFMA phase j, group 1 for V_j);
 2. a buffer is refilled only after every read of its previous tile is done.
 
-The constants and the per-phase lists mirror the kernel in
-fa2_fwd_amd/csrc/attn_bf16.hpp; a change there must be mirrored here.
+The per-phase lists mirror the kernel in fa2_fwd_amd/csrc/attn_bf16.hpp (a
+change there must be mirrored here); the ring depth NBUF is a build option
+there, with AHEAD = NBUF - 1 tiles requested ahead, and both depths the
+kernel is built with are checked.
 """
 
 import pytest
 
-NBUF = 4
-AHEAD = 3
+RINGS = [(4, 3), (5, 4)]  # (NBUF, AHEAD)
 
 
 def intervals(group, phase, j):
@@ -27,43 +29,44 @@ def intervals(group, phase, j):
     return base if phase == "mfma" else base + 1
 
 
-def build_events(ntiles):
+def build_events(ntiles, AHEAD):
     reads = []      # (interval, stream, tile)
     requests = []   # (interval, stream, tile)
     waits = []      # (interval, stream, tile): requester's wait completes this tile
     streams = {0: "K", 1: "V"}
     for g in (0, 1):
         s = streams[g]
-        # prologue (interval -1): request tiles 0..AHEAD-1, wait K_0..K_1 / V_0
+        # prologue (interval -1): request tiles 0..AHEAD-1; group 0 waits for K_0
         for t in range(min(AHEAD, ntiles)):
             requests.append((-1, s, t))
-        for t in (range(0, 2) if g == 0 else range(0, 1)):
-            if t < ntiles:
-                waits.append((-1, s, t))
+        if g == 0:
+            waits.append((-1, s, 0))
         for j in range(ntiles):
             mi = intervals(g, "mfma", j)
             vi = intervals(g, "valu", j)
-            # MFMA phase j: K_j; V_{j-1} for j >= 1 (tile 0 prefetches its own K operands)
+            # MFMA phase j: K_j; V_{j-1} for j >= 1 (tile 0 reads its own K operands)
             reads.append((mi, "K", j))
             if j >= 1:
                 reads.append((mi, "V", j - 1))
-            # VALU phase j: prefetch of MFMA phase j+1 operands, request, wait
+            # end of MFMA phase j: group 0 waits for K_{j+1}, group 1 for V_j
+            need = j + 1 if g == 0 else j
+            for t in range(0, min(need, ntiles - 1) + 1):
+                waits.append((mi, s, t))
+            # VALU phase j: K operands of MFMA phase j+1 read ahead, request of tile j+AHEAD
             if j + 1 < ntiles:
                 reads.append((vi, "K", j + 1))
-                reads.append((vi, "V", j))
             if j + AHEAD < ntiles:
                 requests.append((vi, s, j + AHEAD))
-            need = j + 2 if g == 0 else j + 1
-            for t in range(0, min(need, ntiles - 1) + 1):
-                waits.append((vi, s, t))
         # final P V of the last tile, in the slot of MFMA phase ntiles
         reads.append((intervals(g, "mfma", ntiles), "V", ntiles - 1))
     return reads, requests, waits
 
 
+@pytest.mark.parametrize("ring", RINGS)
 @pytest.mark.parametrize("ntiles", list(range(1, 14)))
-def test_reads_after_completion_and_no_early_refill(ntiles):
-    reads, requests, waits = build_events(ntiles)
+def test_reads_after_completion_and_no_early_refill(ntiles, ring):
+    NBUF, AHEAD = ring
+    reads, requests, waits = build_events(ntiles, AHEAD)
     first_wait = {}
     for i, s, t in waits:
         first_wait[(s, t)] = min(first_wait.get((s, t), i), i)
@@ -86,10 +89,18 @@ def test_reads_after_completion_and_no_early_refill(ntiles):
                 f"{s}{t} requested in interval {i} while {s}{prev} is read in {last_read[(s, prev)]}"
 
 
-def test_wait_counts_within_vmcnt_encoding():
-    # the kernel waits with at most two newer tiles in flight (vmcnt(2*LD))
+@pytest.mark.parametrize("ring", RINGS)
+def test_wait_counts_within_spelled_out_cases(ring):
+    # the kernel spells out waits with at most min(AHEAD - 1, 3) newer tiles
+    # of the group's own stream in flight
+    _, AHEAD = ring
     for ntiles in range(1, 14):
-        for j in range(ntiles):
-            for g, need in ((0, j + 2), (1, j + 1)):
-                after = min(j + AHEAD, ntiles - 1) - need
-                assert after <= 2
+        for j in range(-1, ntiles):
+            if j < 0:
+                checks = [(AHEAD - 1, 0)]  # prologue, group 0: K_0
+            else:
+                newest = j - 1 + AHEAD  # requested by the end of MFMA phase j
+                checks = [(newest, j + 1), (newest, j)]
+            for newest, need in checks:
+                after = min(newest, ntiles - 1) - need
+                assert after <= min(AHEAD - 1, 3)
