@@ -96,16 +96,18 @@ def time_gpu(w, steps: int, warmup: int):
     for _ in range(warmup):
         hfa.attn_fwd(q, k, v, w.scale, out=o, lse=lse, stream=stream)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
+    # One event before each launch and one after the last, all on the launch
+    # stream: their span is the timed region, their gaps the per-launch times.
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(steps):
+    for i in range(steps):
+        events[i].record(stream)
         hfa.attn_fwd(q, k, v, w.scale, out=o, lse=lse, stream=stream)
-    end.record(stream)
+    events[steps].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms = start.elapsed_time(end) / steps
+    ms = events[0].elapsed_time(events[steps]) / steps
+    per_launch = sorted(events[i].elapsed_time(events[i + 1]) for i in range(steps))
     tflops = w.flops / (ms * 1e-3) / 1e12
     peak = MFMA_PEAK_TFLOPS[w.dtype]
     log(f"[bench] {w.describe()}: {ms:.4f} ms/launch, {tflops:.1f} TFLOP/s, {100 * tflops / peak:.1f}% of "
@@ -121,7 +123,67 @@ def time_gpu(w, steps: int, warmup: int):
         "algorithmic_bytes": algorithmic_bytes(w),
         "kernel": kernel_key(w),
     }
-    return {"ms": ms, "tflops": tflops, "wall_s": wall, "roofline": roofline}
+    return {"ms": ms, "tflops": tflops, "wall_s": wall, "roofline": roofline,
+            "ms_median": per_launch[len(per_launch) // 2], "ms_min": per_launch[0]}
+
+
+def _sclk_files():
+    return sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+
+
+def _read_sclk_mhz(path):
+    """Current shader-clock level (MHz) from a pp_dpm_sclk table (the line marked '*')."""
+    try:
+        with open(path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    return float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+    except (OSError, ValueError, IndexError):
+        return None
+    return None
+
+
+def observed_sclk(w, seconds: float):
+    """Median shader clock (MHz) sampled from sysfs while the workload runs untimed.
+
+    The card whose clock is highest during the run is taken as the one in use; None
+    when the tables are not readable."""
+    import threading
+
+    import torch
+
+    import fa2_fwd_amd as hfa
+    from fa2_fwd_amd import workloads as W
+
+    files = _sclk_files()
+    if not files:
+        return None
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in W.workload_inputs(w))
+    samples = {f: [] for f in files}
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            for f in files:
+                mhz = _read_sclk_mhz(f)
+                if mhz is not None:
+                    samples[f].append(mhz)
+            time.sleep(0.005)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    hfa.attn_fwd(q, k, v, w.scale)
+    torch.cuda.synchronize()
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            hfa.attn_fwd(q, k, v, w.scale)
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    medians = [sorted(v)[len(v) // 2] for v in samples.values() if v]
+    return max(medians) if medians else None
 
 
 def cpu_baseline(w, target_s: float):
@@ -238,10 +300,12 @@ def summarize_pmc(w, fetch_dir: str, write_dir: str) -> None:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=5, help="workload number 1-5 (default 5)")
     ap.add_argument("--secondary", type=int, default=3, help="second workload timed beside it (0: none)")
+    ap.add_argument("--no-all-configs", action="store_true", help="skip timing the other workloads")
+    ap.add_argument("--no-sclk", action="store_true", help="skip sampling the shader clock")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
@@ -282,6 +346,26 @@ def main() -> int:
             "config": {"workload": w2.describe(), "B": w2.B, "H": w2.H, "N": w2.N, "d": w2.d},
             "roofline": r2["roofline"],
         }
+    all_configs = None
+    if not args.no_all_configs:
+        all_configs = []
+        for n in sorted(W.CONFIGS):
+            if n == args.config:
+                r = main_res
+            elif secondary is not None and n == args.secondary:
+                r = r2
+            else:
+                r = time_gpu(W.CONFIGS[n], max(10, args.steps // 2), args.warmup)
+            wn = W.CONFIGS[n]
+            all_configs.append({
+                "config": n, "workload": wn.describe(), "dtype": wn.dtype,
+                "ms_per_step": round(r["ms"], 5), "ms_median": round(r["ms_median"], 5),
+                "ms_min": round(r["ms_min"], 5), "tflops": round(r["tflops"], 3),
+                "frac_of_peak": round(r["tflops"] / MFMA_PEAK_TFLOPS[wn.dtype], 4),
+            })
+    sclk = None if args.no_sclk else observed_sclk(w, 0.5)
+    if sclk is not None:
+        log(f"[bench] shader clock during {w.describe()}: {sclk:.0f} MHz (median of sysfs samples)")
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
     props = torch.cuda.get_device_properties(0)
     line = {
@@ -292,6 +376,8 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(main_res["ms"], 5),
+        "ms_median": round(main_res["ms_median"], 5),
+        "ms_min": round(main_res["ms_min"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -301,6 +387,8 @@ def main() -> int:
         "roofline": main_res["roofline"],
         "cpu_baseline": cpu,
         "secondary": secondary,
+        "all_configs": all_configs,
+        "observed_sclk_mhz": sclk,
         "device": getattr(props, "gcnArchName", props.name),
     }
     print(json.dumps(line), flush=True)
