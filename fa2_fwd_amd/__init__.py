@@ -61,7 +61,7 @@ def load_library(path: str | Path | None = None) -> ctypes.CDLL:
     lib.hfa_attn_fwd.restype = ctypes.c_int
     lib.hfa_status_str.argtypes = [ctypes.c_int]
     lib.hfa_status_str.restype = ctypes.c_char_p
-    lib.hfa_block_rows.argtypes = [ctypes.c_int, i64]
+    lib.hfa_block_rows.argtypes = [ctypes.c_int, i64, i64, i64, i64]
     lib.hfa_block_rows.restype = i64
     if path is None:
         _lib = lib
@@ -77,8 +77,8 @@ def hfa_status_str(status: int) -> str:
     return load_library().hfa_status_str(int(status)).decode()
 
 
-def hfa_block_rows(dtype: int, d: int) -> int:
-    return int(load_library().hfa_block_rows(int(dtype), int(d)))
+def hfa_block_rows(dtype: int, B: int, H: int, N: int, d: int) -> int:
+    return int(load_library().hfa_block_rows(int(dtype), int(B), int(H), int(N), int(d)))
 
 
 def _dtype_code(t) -> int:

@@ -51,8 +51,34 @@ struct F32Tile {
   static_assert(KT % 16 == 0, "key tile is a whole number of 16-key MFMA blocks");
 };
 
-__device__ __forceinline__ double max_xor(double x, int m) { return fmax(x, __shfl_xor(x, m)); }
-__device__ __forceinline__ double add_xor(double x, int m) { return x + __shfl_xor(x, m); }
+// The values of x in the lane pair (l, l ^ 16) or (l, l ^ 32), in an order that
+// depends on the lane (use in symmetric operations only).  gfx950's
+// v_permlane16_swap / v_permlane32_swap exchange 16-lane rows on the vector
+// unit; both 32-bit halves of the double go through the same exchange.
+template <int M>
+__device__ __forceinline__ void pair_f64(double x, double& a, double& b) {
+  static_assert(M == 16 || M == 32, "row exchanges of 16 or 32 lanes");
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = static_cast<uint32_t>(u), hi = static_cast<uint32_t>(u >> 32);
+  auto rl = M == 16 ? __builtin_amdgcn_permlane16_swap(lo, lo, false, false)
+                    : __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  auto rh = M == 16 ? __builtin_amdgcn_permlane16_swap(hi, hi, false, false)
+                    : __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  a = __builtin_bit_cast(double, (static_cast<uint64_t>(rh[0]) << 32) | rl[0]);
+  b = __builtin_bit_cast(double, (static_cast<uint64_t>(rh[1]) << 32) | rl[1]);
+}
+template <int M>
+__device__ __forceinline__ double max_xor(double x) {
+  double a, b;
+  pair_f64<M>(x, a, b);
+  return fmax(a, b);
+}
+template <int M>
+__device__ __forceinline__ double add_xor(double x) {
+  double a, b;
+  pair_f64<M>(x, a, b);
+  return a + b;
+}
 
 template <class T>
 __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
@@ -186,8 +212,8 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
       for (int kb = 0; kb < KT / 16; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mx = fmax(mx, s[qb][kb][r]);
-      mx = max_xor(mx, 16);
-      mx = max_xor(mx, 32);
+      mx = max_xor<16>(mx);
+      mx = max_xor<32>(mx);
       // log2-domain running max, rounded up to an integer: exact rescale factors.
       const double m_new = fmax(m2[qb], ceil(mx * c2));
       const float alpha = exp2_hw(static_cast<float>(m2[qb] - m_new));  // 0 on the first tile
@@ -231,7 +257,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
   // ---- epilogue.  acc[qb][n][r] is O[q][64*(n/4) + 16g + 4r + n%4].
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const double l_tot = add_xor(add_xor(l_run[qb], 16), 32);
+    const double l_tot = add_xor<32>(add_xor<16>(l_run[qb]));
     const float inv = static_cast<float>(1.0 / l_tot);
     const int row = qrow0 + qb * 16 + i16;
     if (row < N) {

@@ -25,18 +25,33 @@ using namespace hfa;
 #ifndef HFA_BF16_D64_TILE
 #define HFA_BF16_D64_TILE 1, 8
 #endif
-#ifndef HFA_F32_D64_TILE
-#define HFA_F32_D64_TILE 2, 4, 64
+// fp32, d = 64: 256-row workgroups (two 16-query blocks per wave, 8 waves)
+// where the grid still fills every CU, 128-row ones (one block per wave)
+// otherwise.
+#ifndef HFA_F32_D64_BIG_TILE
+#define HFA_F32_D64_BIG_TILE 2, 8, 64
+#endif
+#ifndef HFA_F32_D64_SMALL_TILE
+#define HFA_F32_D64_SMALL_TILE 1, 8, 64
 #endif
 #ifndef HFA_F32_D128_TILE
 #define HFA_F32_D128_TILE 2, 4, 32
 #endif
 using Bf16D128 = Bf16Tile<128, HFA_BF16_D128_TILE>;
 using Bf16D64 = Bf16Tile<64, HFA_BF16_D64_TILE>;
-using F32D64 = F32Tile<64, HFA_F32_D64_TILE>;
+using F32D64Big = F32Tile<64, HFA_F32_D64_BIG_TILE>;
+using F32D64Small = F32Tile<64, HFA_F32_D64_SMALL_TILE>;
 using F32D128 = F32Tile<128, HFA_F32_D128_TILE>;
 
 constexpr double kLog2e = 1.44269504088896340736;  // 1 / ln 2
+constexpr int64_t kComputeUnits = 256;  // gfx950 (MI350 series): 8 XCDs x 32 CUs
+
+// Whether the fp32, d = 64 shape takes the 256-row tiling: it does when that
+// grid still gives every compute unit a workgroup.
+bool f32_d64_big(int64_t BH, int64_t N) {
+  const int64_t wgs = BH * ((N + F32D64Big::BR - 1) / F32D64Big::BR);
+  return wgs >= kComputeUnits;
+}
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
@@ -131,10 +146,11 @@ hfa_status launch_f32(const void* q, const void* k, const void* v, void* o, floa
 
 extern "C" {
 
-int64_t hfa_block_rows(hfa_dtype dtype, int64_t d) {
+int64_t hfa_block_rows(hfa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t d) {
+  if (B < 1 || H < 1 || N < 1 || B > INT64_MAX / H) return 0;
   if (dtype == HFA_BF16 && d == 128) return Bf16D128::BR;
   if (dtype == HFA_BF16 && d == 64) return Bf16D64::BR;
-  if (dtype == HFA_F32 && d == 64) return F32D64::BR;
+  if (dtype == HFA_F32 && d == 64) return f32_d64_big(B * H, N) ? F32D64Big::BR : F32D64Small::BR;
   if (dtype == HFA_F32 && d == 128) return F32D128::BR;
   return 0;
 }
@@ -185,7 +201,10 @@ hfa_status hfa_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
     if (d == 128) return launch_bf16<Bf16D128>(q, k, v, o, lse, BH, N, scale, st);
     return launch_bf16<Bf16D64>(q, k, v, o, lse, BH, N, scale, st);
   }
-  if (d == 64) return launch_f32<F32D64>(q, k, v, o, lse, BH, N, scale, st);
+  if (d == 64) {
+    if (f32_d64_big(BH, N)) return launch_f32<F32D64Big>(q, k, v, o, lse, BH, N, scale, st);
+    return launch_f32<F32D64Small>(q, k, v, o, lse, BH, N, scale, st);
+  }
   return launch_f32<F32D128>(q, k, v, o, lse, BH, N, scale, st);
 }
 

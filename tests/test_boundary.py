@@ -67,10 +67,22 @@ def test_status_strings_distinct():
 def test_block_rows_table():
     for dt in (hfa.HFA_F32, hfa.HFA_BF16):
         for d in (64, 128):
-            br = hfa.hfa_block_rows(dt, d)
+            br = hfa.hfa_block_rows(dt, 1, 1, 1000, d)
             assert br > 0 and br % 16 == 0
-    assert hfa.hfa_block_rows(hfa.HFA_F32, 96) == 0
-    assert hfa.hfa_block_rows(7, 64) == 0
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 1, 1000, 96) == 0
+    assert hfa.hfa_block_rows(7, 1, 1, 1000, 64) == 0
+    assert hfa.hfa_block_rows(hfa.HFA_BF16, 0, 1, 1000, 128) == 0
+    assert hfa.hfa_block_rows(hfa.HFA_BF16, 1, 1, 0, 128) == 0
+
+
+def test_block_rows_follow_the_shape():
+    # fp32 d=64 takes 256-row workgroups only when they still cover 256 CUs:
+    # B*H*ceil(N/256) >= 256 (the N=2048, B*H=32 workload), else 128 rows.
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 4, 8, 2048, 64) == 256
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 4, 8, 1024, 64) == 128
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 1, 128, 64) == 128
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 256, 200, 64) == 256
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 255, 256, 64) == 128
 
 
 @pytest.mark.parametrize("kw,status", [

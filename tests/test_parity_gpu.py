@@ -126,6 +126,16 @@ def test_peaked_rows(dtype):
     check_case(f"peaked {dtype}", q, k, v, 0.125, dtype)
 
 
+@pytest.mark.parametrize("B,H,N", [(1, 256, 200), (2, 64, 300), (1, 255, 256), (1, 4, 777)])
+def test_f32_d64_both_tilings(B, H, N):
+    # fp32 d=64 takes 256-row workgroups when B*H*ceil(N/256) >= 256, else
+    # 128-row ones; both, with ragged N.
+    br = hfa.hfa_block_rows(hfa.HFA_F32, B, H, N, 64)
+    q, k, v = W.make_inputs(B, H, N, 64, "f32", seed=B * 1000 + H + N, qk_mult=2.0)
+    rows = W.sample_rows(N, 24, seed=N)
+    check_case(f"f32 d=64 B={B} H={H} N={N} (B_r={br})", q, k, v, 0.125, "f32", rows=rows)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_rising_scores(dtype, d):
