@@ -127,6 +127,28 @@ def time_gpu(w, steps: int, warmup: int):
             "ms_median": per_launch[len(per_launch) // 2], "ms_min": per_launch[0]}
 
 
+def graph_time(w, count: int, reps: int):
+    """Per-launch time when `count` launches are replayed from one captured graph."""
+    import torch
+
+    import fa2_fwd_amd as hfa
+    from fa2_fwd_amd import workloads as W
+
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in W.workload_inputs(w))
+    stream = torch.cuda.current_stream(dev)
+    with hfa.AttnGraph(q, k, v, w.scale, count=count) as g:
+        g.launch(stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            g.launch(stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (reps * count)
+
+
 def _sclk_files():
     return sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
 
@@ -357,11 +379,15 @@ def main() -> int:
             else:
                 r = time_gpu(W.CONFIGS[n], max(10, args.steps // 2), args.warmup)
             wn = W.CONFIGS[n]
+            graph_ms = graph_time(wn, 100, 3) if wn.flops < 1e10 else None
+            if graph_ms is not None:
+                log(f"[bench] {wn.describe()}: {graph_ms * 1e3:.2f} us/launch replayed from a graph of 100")
             all_configs.append({
                 "config": n, "workload": wn.describe(), "dtype": wn.dtype,
                 "ms_per_step": round(r["ms"], 5), "ms_median": round(r["ms_median"], 5),
                 "ms_min": round(r["ms_min"], 5), "tflops": round(r["tflops"], 3),
                 "frac_of_peak": round(r["tflops"] / MFMA_PEAK_TFLOPS[wn.dtype], 4),
+                "ms_per_launch_graph": None if graph_ms is None else round(graph_ms, 5),
             })
     sclk = None if args.no_sclk else observed_sclk(w, 0.5)
     if sclk is not None:

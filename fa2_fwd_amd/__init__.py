@@ -30,7 +30,8 @@ HFA_ERR_ALIAS = 6
 HFA_ERR_NO_DEVICE = 7
 HFA_ERR_LAUNCH = 8
 
-EXPORTED = ("hfa_attn_fwd", "hfa_status_str", "hfa_block_rows")
+EXPORTED = ("hfa_attn_fwd", "hfa_status_str", "hfa_block_rows", "hfa_attn_fwd_graph_create", "hfa_graph_launch",
+            "hfa_graph_destroy")
 
 _lib = None
 
@@ -63,6 +64,13 @@ def load_library(path: str | Path | None = None) -> ctypes.CDLL:
     lib.hfa_status_str.restype = ctypes.c_char_p
     lib.hfa_block_rows.argtypes = [ctypes.c_int, i64, i64, i64, i64]
     lib.hfa_block_rows.restype = i64
+    lib.hfa_attn_fwd_graph_create.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
+                                              i64, ctypes.POINTER(vp)]
+    lib.hfa_attn_fwd_graph_create.restype = ctypes.c_int
+    lib.hfa_graph_launch.argtypes = [vp, vp]
+    lib.hfa_graph_launch.restype = ctypes.c_int
+    lib.hfa_graph_destroy.argtypes = [vp]
+    lib.hfa_graph_destroy.restype = None
     if path is None:
         _lib = lib
     return lib
@@ -81,6 +89,22 @@ def hfa_block_rows(dtype: int, B: int, H: int, N: int, d: int) -> int:
     return int(load_library().hfa_block_rows(int(dtype), int(B), int(H), int(N), int(d)))
 
 
+def hfa_attn_fwd_graph_create(q, k, v, o, lse, B, H, N, d, scale, dtype, count):
+    """Raw C-ABI call; returns (status, graph handle or None)."""
+    h = ctypes.c_void_p()
+    st = load_library().hfa_attn_fwd_graph_create(q, k, v, o, lse, B, H, N, d, scale, dtype, count,
+                                                 ctypes.byref(h))
+    return st, h.value
+
+
+def hfa_graph_launch(graph, stream) -> int:
+    return load_library().hfa_graph_launch(graph, stream)
+
+
+def hfa_graph_destroy(graph) -> None:
+    load_library().hfa_graph_destroy(graph)
+
+
 def _dtype_code(t) -> int:
     import torch
 
@@ -91,15 +115,8 @@ def _dtype_code(t) -> int:
     raise ValueError(f"attn_fwd supports float32 and bfloat16, got {t.dtype}")
 
 
-def attn_fwd(q, k, v, scale: float | None = None, out=None, lse=None, stream=None):
-    """O, LSE = attention forward of device tensors q, k, v of shape [B, H, N, d].
-
-    ``scale`` defaults to 1/sqrt(d).  ``out`` ([B,H,N,d], q's dtype) and ``lse``
-    ([B,H,N] float32) may be given to write into caller buffers.  The kernel is
-    enqueued on ``stream`` (default: torch's current stream) and not waited for.
-    Raises ValueError on dtype, shape, device or contiguity mismatch and
-    HfaError on a library error.
-    """
+def _prepare(q, k, v, scale, out, lse):
+    """Checks of attn_fwd's tensor arguments; allocates out / lse when None."""
     import torch
 
     tensors = (q, k, v)
@@ -125,12 +142,84 @@ def attn_fwd(q, k, v, scale: float | None = None, out=None, lse=None, stream=Non
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     elif lse.shape != (B, H, N) or lse.dtype != torch.float32 or lse.device != q.device or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    return B, H, N, d, code, float(scale), out, lse
+
+
+def _stream_handle(stream, device):
+    import torch
+
     if stream is None:
-        stream = torch.cuda.current_stream(q.device)
-    handle = stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def attn_fwd(q, k, v, scale: float | None = None, out=None, lse=None, stream=None):
+    """O, LSE = attention forward of device tensors q, k, v of shape [B, H, N, d].
+
+    ``scale`` defaults to 1/sqrt(d).  ``out`` ([B,H,N,d], q's dtype) and ``lse``
+    ([B,H,N] float32) may be given to write into caller buffers.  The kernel is
+    enqueued on ``stream`` (default: torch's current stream) and not waited for.
+    Raises ValueError on dtype, shape, device or contiguity mismatch and
+    HfaError on a library error.
+    """
+    import torch
+
+    B, H, N, d, code, scale, out, lse = _prepare(q, k, v, scale, out, lse)
+    handle = _stream_handle(stream, q.device)
     with torch.cuda.device(q.device):
         st = hfa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                          B, H, N, d, float(scale), code, handle)
+                          B, H, N, d, scale, code, handle)
     if st != HFA_OK:
         raise HfaError(st)
     return out, lse
+
+
+class AttnGraph:
+    """``count`` attention forwards of fixed tensors, captured once into a HIP graph.
+
+    ``launch()`` replays all of them with one driver call (see
+    hfa_attn_fwd_graph_create in include/hfa.h).  ``out`` and ``lse`` are the
+    buffers every replay writes.  The tensors must outlive the graph; use
+    ``close()`` (or ``with``) to release it once its replays are done.
+    """
+
+    def __init__(self, q, k, v, scale: float | None = None, out=None, lse=None, count: int = 1):
+        import torch
+
+        B, H, N, d, code, scale, out, lse = _prepare(q, k, v, scale, out, lse)
+        self.q, self.k, self.v, self.out, self.lse = q, k, v, out, lse
+        self.device = q.device
+        with torch.cuda.device(q.device):
+            st, h = hfa_attn_fwd_graph_create(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                              lse.data_ptr(), B, H, N, d, scale, code, int(count))
+        if st != HFA_OK:
+            raise HfaError(st)
+        self._graph = h
+
+    def launch(self, stream=None):
+        import torch
+
+        if self._graph is None:
+            raise ValueError("graph already closed")
+        with torch.cuda.device(self.device):
+            st = hfa_graph_launch(self._graph, _stream_handle(stream, self.device))
+        if st != HFA_OK:
+            raise HfaError(st)
+        return self.out, self.lse
+
+    def close(self):
+        if self._graph is not None:
+            hfa_graph_destroy(self._graph)
+            self._graph = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstring>
 #include <mutex>
+#include <new>
 
 #include "hfa.h"
 #include "attn_bf16.hpp"
@@ -106,13 +107,16 @@ ScaleArgs split_scale(float scale) {
   return {std::fabs(s) * kLog2e, s < 0 ? -1 : 1};
 }
 
+// With launch == false only the one-time kernel attributes are set (before a
+// stream capture, which must contain nothing but the launches).
 template <class T>
 hfa_status launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH,
-                       int64_t N, float scale, hipStream_t stream) {
+                       int64_t N, float scale, hipStream_t stream, bool launch) {
   static std::once_flag flag;
   static hipError_t err = hipSuccess;
   auto kernel = attn_fwd_bf16_kernel<T>;
   if (ensure_lds(kernel, T::LDS_BYTES, flag, err) != HFA_OK) return HFA_ERR_LAUNCH;
+  if (!launch) return HFA_OK;
   const int64_t n_qt = (N + T::BR - 1) / T::BR;
   const int64_t total = BH * n_qt;
   if (total > INT_MAX) return HFA_ERR_SHAPE;
@@ -126,11 +130,12 @@ hfa_status launch_bf16(const void* q, const void* k, const void* v, void* o, flo
 
 template <class T>
 hfa_status launch_f32(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH,
-                      int64_t N, float scale, hipStream_t stream) {
+                      int64_t N, float scale, hipStream_t stream, bool launch) {
   static std::once_flag flag;
   static hipError_t err = hipSuccess;
   auto kernel = attn_fwd_f32_kernel<T>;
   if (ensure_lds(kernel, T::LDS_BYTES, flag, err) != HFA_OK) return HFA_ERR_LAUNCH;
+  if (!launch) return HFA_OK;
   const int64_t n_qt = (N + T::BR - 1) / T::BR;
   const int64_t total = BH * n_qt;
   if (total > INT_MAX) return HFA_ERR_SHAPE;
@@ -142,7 +147,53 @@ hfa_status launch_f32(const void* q, const void* k, const void* v, void* o, floa
   return hipGetLastError() == hipSuccess ? HFA_OK : HFA_ERR_LAUNCH;
 }
 
+// Every argument check of hfa_attn_fwd, before any HIP call.
+hfa_status validate(const void* q, const void* k, const void* v, const void* o, const float* lse, int64_t B,
+                    int64_t H, int64_t N, int64_t d, float scale, hfa_dtype dtype) {
+  if (dtype != HFA_F32 && dtype != HFA_BF16) return HFA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return HFA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !o || !lse) return HFA_ERR_NULL;
+  if (B < 1 || H < 1 || N < 1) return HFA_ERR_SHAPE;
+  if (N > INT_MAX / d) return HFA_ERR_SHAPE;
+  if (B > INT64_MAX / H) return HFA_ERR_SHAPE;
+  const int64_t BH = B * H;
+  if (BH > INT_MAX) return HFA_ERR_SHAPE;
+  if (!std::isfinite(scale)) return HFA_ERR_SCALE;
+  auto misaligned = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; };
+  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(lse, 4))
+    return HFA_ERR_ALIGN;
+  const size_t elt = dtype == HFA_F32 ? 4 : 2;
+  const size_t n_elems = static_cast<size_t>(BH) * static_cast<size_t>(N) * static_cast<size_t>(d);
+  const size_t bytes = n_elems * elt;
+  const size_t lse_bytes = static_cast<size_t>(BH) * static_cast<size_t>(N) * sizeof(float);
+  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes) ||
+      overlaps(lse, lse_bytes, q, bytes) || overlaps(lse, lse_bytes, k, bytes) ||
+      overlaps(lse, lse_bytes, v, bytes) || overlaps(lse, lse_bytes, o, bytes))
+    return HFA_ERR_ALIAS;
+  return HFA_OK;
+}
+
+// Kernel selection for a validated call; enqueues it on `stream` when launch.
+hfa_status dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t N,
+                    int64_t d, float scale, hfa_dtype dtype, hipStream_t st, bool launch) {
+  if (dtype == HFA_BF16) {
+    if (d == 128) return launch_bf16<Bf16D128>(q, k, v, o, lse, BH, N, scale, st, launch);
+    return launch_bf16<Bf16D64>(q, k, v, o, lse, BH, N, scale, st, launch);
+  }
+  if (d == 64) {
+    if (f32_d64_big(BH, N)) return launch_f32<F32D64Big>(q, k, v, o, lse, BH, N, scale, st, launch);
+    return launch_f32<F32D64Small>(q, k, v, o, lse, BH, N, scale, st, launch);
+  }
+  return launch_f32<F32D128>(q, k, v, o, lse, BH, N, scale, st, launch);
+}
+
 }  // namespace
+
+// A captured and instantiated sequence of attention launches.
+struct hfa_graph_s {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
 
 extern "C" {
 
@@ -172,40 +223,75 @@ const char* hfa_status_str(hfa_status s) {
 
 hfa_status hfa_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
                         int64_t H, int64_t N, int64_t d, float scale, hfa_dtype dtype, void* stream) {
-  if (dtype != HFA_F32 && dtype != HFA_BF16) return HFA_ERR_UNSUPPORTED;
-  if (d != 64 && d != 128) return HFA_ERR_UNSUPPORTED;
-  if (!q || !k || !v || !o || !lse) return HFA_ERR_NULL;
-  if (B < 1 || H < 1 || N < 1) return HFA_ERR_SHAPE;
-  if (N > INT_MAX / d) return HFA_ERR_SHAPE;
-  if (B > INT64_MAX / H) return HFA_ERR_SHAPE;
-  const int64_t BH = B * H;
-  if (BH > INT_MAX) return HFA_ERR_SHAPE;
-  if (!std::isfinite(scale)) return HFA_ERR_SCALE;
-  auto misaligned = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; };
-  if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(lse, 4))
-    return HFA_ERR_ALIGN;
-  const size_t elt = dtype == HFA_F32 ? 4 : 2;
-  const size_t n_elems = static_cast<size_t>(BH) * static_cast<size_t>(N) * static_cast<size_t>(d);
-  const size_t bytes = n_elems * elt;
-  const size_t lse_bytes = static_cast<size_t>(BH) * static_cast<size_t>(N) * sizeof(float);
-  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes) ||
-      overlaps(lse, lse_bytes, q, bytes) || overlaps(lse, lse_bytes, k, bytes) ||
-      overlaps(lse, lse_bytes, v, bytes) || overlaps(lse, lse_bytes, o, bytes))
-    return HFA_ERR_ALIAS;
-
+  const hfa_status st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype);
+  if (st != HFA_OK) return st;
   const hfa_status dev = check_device();
   if (dev != HFA_OK) return dev;
+  return dispatch(q, k, v, o, lse, B * H, N, d, scale, dtype, static_cast<hipStream_t>(stream), true);
+}
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (dtype == HFA_BF16) {
-    if (d == 128) return launch_bf16<Bf16D128>(q, k, v, o, lse, BH, N, scale, st);
-    return launch_bf16<Bf16D64>(q, k, v, o, lse, BH, N, scale, st);
+hfa_status hfa_attn_fwd_graph_create(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     int64_t B, int64_t H, int64_t N, int64_t d, float scale, hfa_dtype dtype,
+                                     int64_t count, hfa_graph* out) {
+  if (!out) return HFA_ERR_NULL;
+  *out = nullptr;
+  const hfa_status st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype);
+  if (st != HFA_OK) return st;
+  if (count < 1 || count > (1 << 20)) return HFA_ERR_SHAPE;
+  const hfa_status dev = check_device();
+  if (dev != HFA_OK) return dev;
+  const int64_t BH = B * H;
+  if (dispatch(q, k, v, o, lse, BH, N, d, scale, dtype, nullptr, false) != HFA_OK) return HFA_ERR_LAUNCH;
+
+  hipStream_t s = nullptr;
+  if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
+    (void)hipGetLastError();
+    return HFA_ERR_LAUNCH;
   }
-  if (d == 64) {
-    if (f32_d64_big(BH, N)) return launch_f32<F32D64Big>(q, k, v, o, lse, BH, N, scale, st);
-    return launch_f32<F32D64Small>(q, k, v, o, lse, BH, N, scale, st);
+  hfa_status result = HFA_OK;
+  hipGraph_t graph = nullptr;
+  if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+    result = HFA_ERR_LAUNCH;
+  } else {
+    for (int64_t i = 0; i < count && result == HFA_OK; ++i)
+      result = dispatch(q, k, v, o, lse, BH, N, d, scale, dtype, s, true);
+    if (hipStreamEndCapture(s, &graph) != hipSuccess && result == HFA_OK) result = HFA_ERR_LAUNCH;
   }
-  return launch_f32<F32D128>(q, k, v, o, lse, BH, N, scale, st);
+  hipGraphExec_t exec = nullptr;
+  if (result == HFA_OK && hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0) != hipSuccess)
+    result = HFA_ERR_LAUNCH;
+  (void)hipStreamDestroy(s);
+  if (result != HFA_OK) {
+    if (graph) (void)hipGraphDestroy(graph);
+    (void)hipGetLastError();
+    return result;
+  }
+  hfa_graph g = new (std::nothrow) hfa_graph_s;
+  if (!g) {
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(graph);
+    return HFA_ERR_LAUNCH;
+  }
+  g->graph = graph;
+  g->exec = exec;
+  *out = g;
+  return HFA_OK;
+}
+
+hfa_status hfa_graph_launch(hfa_graph g, void* stream) {
+  if (!g) return HFA_ERR_NULL;
+  if (hipGraphLaunch(g->exec, static_cast<hipStream_t>(stream)) != hipSuccess) {
+    (void)hipGetLastError();
+    return HFA_ERR_LAUNCH;
+  }
+  return HFA_OK;
+}
+
+void hfa_graph_destroy(hfa_graph g) {
+  if (!g) return;
+  (void)hipGraphExecDestroy(g->exec);
+  (void)hipGraphDestroy(g->graph);
+  delete g;
 }
 
 }  // extern "C"

@@ -22,9 +22,11 @@
  * products on bf16 matrix cores with fp32 accumulation, softmax in fp32,
  * P rounded to bf16 (round-to-nearest-even) for P V, O rounded to bf16 once.
  *
- * Ownership.  The caller owns every buffer; the library allocates nothing,
+ * Ownership.  The caller owns every buffer; hfa_attn_fwd allocates nothing,
  * keeps no state between calls and never holds an N x N buffer.  All pointers
- * passed to hfa_attn_fwd are device pointers on the current HIP device.
+ * passed to it are device pointers on the current HIP device.  The graph
+ * functions at the end create host-side driver objects owned by the returned
+ * handle.
  *
  * Errors.  Every argument is validated before any HIP call is made; on a
  * validation error the call returns the status and leaves o and lse
@@ -87,6 +89,37 @@ const char* hfa_status_str(hfa_status s);
  * head dim or a shape with B, H or N below 1.  Needs no device and makes no
  * HIP call. */
 int64_t hfa_block_rows(hfa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t d);
+
+/* Graph replay for launch-bound shapes.  Following the "CUDA Graphs" part
+ * of section 4 of the neuralmasteryai page "Hardware Acceleration & Custom
+ * Kernels" (per-kernel CPU dispatch costs microseconds; a graph captured once
+ * is replayed with one driver call), hfa_attn_fwd_graph_create records
+ * `count` identical hfa_attn_fwd calls into a HIP graph and instantiates it.
+ *
+ *   Arguments q ... dtype are those of hfa_attn_fwd and are validated the same
+ *   way, with the same status codes, before any HIP call.  The buffers must
+ *   stay allocated while the graph exists; every replay rereads q, k, v and
+ *   rewrites o and lse.
+ *   count  number of launches recorded, 1 <= count <= 2^20 (else HFA_ERR_SHAPE).
+ *   out    receives the graph handle (NULL on failure); HFA_ERR_NULL if NULL.
+ *
+ * The capture runs on a private stream of default priority that is destroyed
+ * before returning; the graph holds host-side driver objects only, no device
+ * buffers.  HFA_ERR_LAUNCH if a HIP graph call fails.  The graph belongs to
+ * the device current at creation. */
+typedef struct hfa_graph_s* hfa_graph;
+hfa_status hfa_attn_fwd_graph_create(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                                     hfa_dtype dtype, int64_t count, hfa_graph* out);
+
+/* Enqueue one replay of the whole graph on `stream` (a hipStream_t of the
+ * graph's device; NULL selects the null stream).  HFA_ERR_NULL for a NULL
+ * graph, HFA_ERR_LAUNCH if the launch is refused. */
+hfa_status hfa_graph_launch(hfa_graph g, void* stream);
+
+/* Release a graph (NULL is ignored).  No replay of it may still be pending:
+ * synchronise its streams first. */
+void hfa_graph_destroy(hfa_graph g);
 
 #ifdef __cplusplus
 }

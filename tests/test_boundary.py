@@ -140,3 +140,36 @@ def test_python_binding_value_errors():
         hfa.attn_fwd(q.double(), q.double(), q.double())
     with pytest.raises(ValueError):
         hfa.attn_fwd(q[0], q[0], q[0])
+
+
+def _graph_create(count=1, **kw):
+    a = dict(GOOD, B=1, H=1, N=128, d=64, scale=0.125, dtype=hfa.HFA_F32)
+    a.update(kw)
+    return hfa.hfa_attn_fwd_graph_create(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                                         a["d"], a["scale"], a["dtype"], count)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), hfa.HFA_ERR_UNSUPPORTED),
+    (dict(dtype=5), hfa.HFA_ERR_UNSUPPORTED),
+    (dict(q=None), hfa.HFA_ERR_NULL),
+    (dict(N=0), hfa.HFA_ERR_SHAPE),
+    (dict(scale=float("inf")), hfa.HFA_ERR_SCALE),
+    (dict(o=0x400004), hfa.HFA_ERR_ALIGN),
+    (dict(lse=0x100010), hfa.HFA_ERR_ALIAS),
+    (dict(count=0), hfa.HFA_ERR_SHAPE),
+    (dict(count=(1 << 20) + 1), hfa.HFA_ERR_SHAPE),
+])
+def test_graph_create_validates_like_attn_fwd(kw, status):
+    count = kw.pop("count", 1)
+    st, h = _graph_create(count=count, **kw)
+    assert st == status and h is None
+
+
+def test_graph_null_handles():
+    lib = hfa.load_library()
+    assert hfa.hfa_graph_launch(None, None) == hfa.HFA_ERR_NULL
+    hfa.hfa_graph_destroy(None)  # ignored
+    import ctypes
+    assert lib.hfa_attn_fwd_graph_create(0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 1, 1, 128, 64,
+                                         0.125, hfa.HFA_F32, 1, None) == hfa.HFA_ERR_NULL
