@@ -17,6 +17,11 @@ section "Fusion", the stable row softmax):
 ``attn_fwd_online`` computes the same quantities by the online normalisation
 identity of that section 2, step 2, tile by tile over the keys.
 
+``softmax_rows`` is the standalone stable row softmax of that chapter's
+"Fusion" section (y = exp(x - max) / sum, per row of a float32 matrix);
+``softmax_rows_online`` takes the row max and sum in one sweep by the same
+running identity, over chunks of any width.
+
 Inputs are numpy arrays of shape [B, H, N, d]: ``float32`` for fp32 data, or
 ``uint16`` holding bf16 bit patterns.  Outputs are fp64.
 """
@@ -73,6 +78,10 @@ class OracleLib:
         lib.hfa_ref_attn_fwd_online.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, i64, i64,
                                                 ctypes.c_double, i64, vp, i64, vp, vp, ctypes.c_int]
         lib.hfa_ref_attn_fwd_online.restype = ctypes.c_int
+        lib.hfa_ref_softmax_rows.argtypes = [vp, i64, i64, vp, i64, vp, ctypes.c_int]
+        lib.hfa_ref_softmax_rows.restype = ctypes.c_int
+        lib.hfa_ref_softmax_rows_online.argtypes = [vp, i64, i64, i64, vp, i64, vp, ctypes.c_int]
+        lib.hfa_ref_softmax_rows_online.restype = ctypes.c_int
         self.lib = lib
         self.path = str(path)
 
@@ -97,6 +106,34 @@ class OracleLib:
         if rc != 0:
             raise ValueError("oracle rejected its arguments (%s)" % fn_name)
         return o, lse
+
+    def _softmax(self, x, rows, threads, chunk=None):
+        x = np.ascontiguousarray(x)
+        if x.dtype != np.float32 or x.ndim != 2:
+            raise ValueError("softmax oracle input is a float32 [R, C] array")
+        R, C = x.shape
+        rows_arr = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n = R if rows_arr is None else rows_arr.shape[0]
+        y = np.empty((n, C), dtype=np.float64)
+        thr = int(threads) if threads else default_threads()
+        rp = None if rows_arr is None else rows_arr.ctypes.data
+        if chunk is None:
+            rc = self.lib.hfa_ref_softmax_rows(x.ctypes.data, R, C, rp, n if rows_arr is not None else 0,
+                                               y.ctypes.data, thr)
+        else:
+            rc = self.lib.hfa_ref_softmax_rows_online(x.ctypes.data, R, C, int(chunk), rp,
+                                                      n if rows_arr is not None else 0, y.ctypes.data, thr)
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments (softmax)")
+        return y
+
+    def softmax_rows(self, x, rows=None, threads=0):
+        """Row softmax of a float32 [R, C] array in fp64 (definition form).  Returns [R or len(rows), C]."""
+        return self._softmax(x, rows, threads)
+
+    def softmax_rows_online(self, x, chunk, rows=None, threads=0):
+        """Row softmax with (max, sum) taken by the running identity over chunks of ``chunk`` columns."""
+        return self._softmax(x, rows, threads, chunk=chunk)
 
     def attn_fwd(self, q, k, v, scale, rows=None, threads=0):
         """Definition-form attention forward in fp64.  Returns (O [B,H,R,d], LSE [B,H,R])."""
@@ -130,3 +167,13 @@ def attn_fwd(q, k, v, scale, rows=None, threads=0):
 def attn_fwd_online(q, k, v, scale, tile, rows=None, threads=0):
     """Online-normalisation form over key tiles of width ``tile`` (fp64)."""
     return default().attn_fwd_online(q, k, v, scale, tile, rows, threads)
+
+
+def softmax_rows(x, rows=None, threads=0):
+    """Row softmax of a float32 [R, C] array in fp64 (definition form)."""
+    return default().softmax_rows(x, rows, threads)
+
+
+def softmax_rows_online(x, chunk, rows=None, threads=0):
+    """Row softmax in fp64 with (max, sum) by the running identity over chunks of ``chunk`` columns."""
+    return default().softmax_rows_online(x, chunk, rows, threads)

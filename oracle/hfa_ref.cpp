@@ -29,8 +29,22 @@
 //                           page states it.  Used only to pin the identity
 //                           against the definition.
 //
-// Both also return the row log-sum-exp LSE_i = ln(sum_j exp(s_ij)) of the
-// scaled scores (natural log).  The pages do not define it; it is the plain
+// Two more for the standalone row softmax (book chapter "Triton and kernel
+// fusion", section "Fusion", and its stretch exercise on rows wider than one
+// block):
+//
+//  hfa_ref_softmax_rows         y_ij = exp(x_ij - m_i) / sum_j exp(x_ij - m_i),
+//                               m_i = max_j x_ij, over fp32 rows widened to fp64.
+//
+//  hfa_ref_softmax_rows_online  the same, with (m_i, l_i) taken in one sweep by
+//                               the running-max / running-sum identity (the
+//                               neuralmasteryai section 2, step 2 recurrence)
+//                               over chunks of `chunk` columns; chunk == 1 is
+//                               the scalar recurrence.  Used only to pin the
+//                               identity against the definition.
+//
+// Both attention entry points also return the row log-sum-exp
+// LSE_i = ln(sum_j exp(s_ij)) of the scaled scores (natural log).  The pages do not define it; it is the plain
 // reading: the running max plus the log of the running denominator.
 //
 // Layout: q, k, v are contiguous [B, H, N, d].  `rows` (may be NULL) selects
@@ -192,9 +206,88 @@ int check_and_run(const void* q, const void* k, const void* v, int dtype, int64_
   return 0;
 }
 
+// ---- standalone row softmax -------------------------------------------------
+
+// Definition form of one row: max, exponentials, sum, divide (fp64).
+void softmax_row_direct(const float* x, int64_t C, double* y) {
+  double m = -INFINITY;
+  for (int64_t j = 0; j < C; ++j) m = std::max(m, static_cast<double>(x[j]));
+  double l = 0.0;
+  for (int64_t j = 0; j < C; ++j) {
+    y[j] = std::exp(static_cast<double>(x[j]) - m);
+    l += y[j];
+  }
+  for (int64_t j = 0; j < C; ++j) y[j] /= l;
+}
+
+// One sweep for (m, l) by the running identity over chunks, then the outputs:
+// for each chunk, m_new = max(m, chunk max), l = l * exp(m - m_new) +
+// sum over the chunk of exp(x - m_new).
+void softmax_row_online(const float* x, int64_t C, int64_t chunk, double* y) {
+  double m = -INFINITY, l = 0.0;
+  for (int64_t b = 0; b < C; b += chunk) {
+    const int64_t e = std::min(C, b + chunk);
+    double cm = -INFINITY;
+    for (int64_t j = b; j < e; ++j) cm = std::max(cm, static_cast<double>(x[j]));
+    const double m_new = std::max(m, cm);
+    double cs = 0.0;
+    for (int64_t j = b; j < e; ++j) cs += std::exp(static_cast<double>(x[j]) - m_new);
+    l = (l == 0.0 ? 0.0 : l * std::exp(m - m_new)) + cs;
+    m = m_new;
+  }
+  for (int64_t j = 0; j < C; ++j) y[j] = std::exp(static_cast<double>(x[j]) - m) / l;
+}
+
+int softmax_check_and_run(const float* x, int64_t R, int64_t C, int64_t chunk, const int64_t* rows,
+                          int64_t n_rows, double* y, int threads) {
+  if (!x || !y || R < 1 || C < 1 || chunk < 0) return -1;
+  const int64_t n = rows ? n_rows : R;
+  if (n < 0) return -1;
+  if (rows)
+    for (int64_t r = 0; r < n_rows; ++r)
+      if (rows[r] < 0 || rows[r] >= R) return -1;
+  for (int64_t i = 0; i < (rows ? n_rows : R); ++i) {
+    const float* row = x + (rows ? rows[i] : i) * C;
+    for (int64_t j = 0; j < C; ++j)
+      if (!std::isfinite(row[j])) return -1;
+  }
+  if (threads < 1) threads = static_cast<int>(std::max(1u, std::thread::hardware_concurrency()));
+  auto worker = [&](int64_t b, int64_t e) {
+    for (int64_t i = b; i < e; ++i) {
+      const float* row = x + (rows ? rows[i] : i) * C;
+      if (chunk == 0)
+        softmax_row_direct(row, C, y + i * C);
+      else
+        softmax_row_online(row, C, chunk, y + i * C);
+    }
+  };
+  const int64_t per = (n + threads - 1) / threads;
+  std::vector<std::thread> pool;
+  for (int t = 0; t < threads; ++t) {
+    const int64_t b = t * per, e = std::min(n, b + per);
+    if (b < e) pool.emplace_back(worker, b, e);
+  }
+  for (auto& th : pool) th.join();
+  return 0;
+}
+
 }  // namespace
 
 extern "C" {
+
+// x: fp32 [R, C] contiguous; rows (may be NULL) selects the rows computed;
+// y: fp64 [n_rows or R, C].  0 on success, -1 on an invalid argument
+// (non-finite inputs included).
+int hfa_ref_softmax_rows(const float* x, int64_t R, int64_t C, const int64_t* rows, int64_t n_rows, double* y,
+                         int threads) {
+  return softmax_check_and_run(x, R, C, 0, rows, n_rows, y, threads);
+}
+
+int hfa_ref_softmax_rows_online(const float* x, int64_t R, int64_t C, int64_t chunk, const int64_t* rows,
+                                int64_t n_rows, double* y, int threads) {
+  if (chunk < 1) return -1;
+  return softmax_check_and_run(x, R, C, chunk, rows, n_rows, y, threads);
+}
 
 int hfa_ref_attn_fwd(const void* q, const void* k, const void* v, int dtype, int64_t B, int64_t H,
                      int64_t N, int64_t d, double scale, const int64_t* rows, int64_t n_rows,

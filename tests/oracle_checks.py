@@ -302,3 +302,123 @@ def check_golden_exact_rational(orc):
 
 
 ALL_CHECKS.append(check_golden_exact_rational)
+
+
+# ---- standalone row softmax (book chapter "Triton and kernel fusion",
+# section "Fusion": subtract the row max, exponentiate, sum, divide; stretch
+# exercise: rows wider than one block by a running max and sum).
+
+def _srand(shape, seed, scale=1.0):
+    return _rand(shape, seed, scale)
+
+
+# S1 -- every row is a probability vector.
+def check_s1_softmax_rows_stochastic(orc):
+    x = _srand((6, 1000), 21, 10.0)
+    y = orc.softmax_rows(x)
+    assert np.all(y >= 0) and np.all(y <= 1)
+    np.testing.assert_allclose(y.sum(axis=1), 1.0, rtol=0, atol=1e-13)
+
+
+# S2 -- a constant row gives the uniform distribution.
+def check_s2_softmax_constant_row(orc):
+    x = np.full((3, 777), 3.25, np.float32)
+    x[1] = -40.0
+    np.testing.assert_allclose(orc.softmax_rows(x), 1.0 / 777, rtol=1e-14, atol=0)
+
+
+# S3 -- two distinct values: C-1 copies of a and one b, closed form
+# y_b = 1 / (1 + (C-1) e^(a-b)), y_a = e^(a-b) y_b.
+def check_s3_softmax_two_values(orc):
+    C, a, b, pos = 301, 1.5, 4.0, 137
+    x = np.full((1, C), a, np.float32)
+    x[0, pos] = b
+    y = orc.softmax_rows(x)[0]
+    yb = 1.0 / (1.0 + (C - 1) * math.exp(a - b))
+    np.testing.assert_allclose(y[pos], yb, rtol=1e-14)
+    np.testing.assert_allclose(np.delete(y, pos), math.exp(a - b) * yb, rtol=1e-14)
+
+
+# S4 -- shifting a row by a constant changes nothing (exact fp32 shift).
+def check_s4_softmax_shift_invariance(orc):
+    rng = np.random.default_rng(24)
+    x = (rng.integers(-80, 80, size=(4, 513)) / 8.0).astype(np.float32)
+    y0 = orc.softmax_rows(x)
+    y1 = orc.softmax_rows((x + np.float32(37.0)).astype(np.float32))
+    np.testing.assert_allclose(y1, y0, rtol=0, atol=1e-15)
+
+
+# S5 -- magnitudes where exp overflows without the max subtraction.
+def check_s5_softmax_large_magnitudes(orc):
+    x = (_srand((3, 400), 25, 30.0) + np.float32(750.0)).astype(np.float32)
+    y = orc.softmax_rows(x)
+    assert np.all(np.isfinite(y))
+    from scipy.special import softmax as sp_softmax
+    np.testing.assert_allclose(y, sp_softmax(x.astype(np.float64), axis=1), rtol=0, atol=1e-14)
+
+
+# S6 -- independent library routine, rows of the chapter's width (32000) and
+# wider than its one-block limit (65536).  The fp64 row sums of C terms carry
+# up to about C * 2^-53 relative rounding in either routine: rtol 5e-13.
+def check_s6_softmax_library_crosscheck(orc):
+    from scipy.special import softmax as sp_softmax
+    for shape, seed in (((3, 32000), 26), ((2, 70001), 27)):
+        x = _srand(shape, seed, 6.0)
+        np.testing.assert_allclose(orc.softmax_rows(x), sp_softmax(x.astype(np.float64), axis=1),
+                                   rtol=5e-13, atol=0)
+
+
+# S7 -- the running (max, sum) identity over any chunking equals the definition.
+def check_s7_softmax_online_equals_direct(orc):
+    x = _srand((3, 1000), 28, 12.0)
+    y = orc.softmax_rows(x)
+    for chunk in (1, 5, 64, 999, 1000, 4096):
+        # the rescale factors add a few roundings: agreement to 1e-13 relative
+        np.testing.assert_allclose(orc.softmax_rows_online(x, chunk), y, rtol=1e-13, atol=0)
+
+
+# S8 -- a row sample gives exactly those rows of the full result.
+def check_s8_softmax_sampled_rows(orc):
+    x = _srand((9, 300), 29, 5.0)
+    full = orc.softmax_rows(x)
+    rows = [7, 0, 8, 3]
+    np.testing.assert_array_equal(orc.softmax_rows(x, rows=rows), full[rows])
+
+
+# S9 -- one element g ~ 60 above the rest (g the gap in the fp32 data):
+# one-hot within (C-1) e^-g, every other weight <= e^-g.
+def check_s9_softmax_dominance(orc):
+    C = 1000
+    x = _srand((1, C), 30, 1.0)
+    x[0, 321] = x[0].max() + 60.0
+    gap = float(x[0, 321]) - float(np.delete(x[0], 321).max())
+    y = orc.softmax_rows(x)[0]
+    assert abs(y[321] - 1.0) <= (C - 1) * math.exp(-gap)
+    assert np.delete(y, 321).max() <= math.exp(-gap) * (1 + 1e-12)
+
+
+def check_s10_softmax_rejects_bad_arguments(orc):
+    x = _srand((2, 10), 31)
+    bad = x.copy()
+    bad[1, 3] = np.nan
+    with pytest.raises(ValueError):
+        orc.softmax_rows(bad)
+    with pytest.raises(ValueError):
+        orc.softmax_rows(x, rows=[0, 2])
+    with pytest.raises(ValueError):
+        orc.softmax_rows_online(x, 0)
+
+
+SOFTMAX_CHECKS = [
+    check_s1_softmax_rows_stochastic,
+    check_s2_softmax_constant_row,
+    check_s3_softmax_two_values,
+    check_s4_softmax_shift_invariance,
+    check_s5_softmax_large_magnitudes,
+    check_s6_softmax_library_crosscheck,
+    check_s7_softmax_online_equals_direct,
+    check_s8_softmax_sampled_rows,
+    check_s9_softmax_dominance,
+    check_s10_softmax_rejects_bad_arguments,
+]
+ALL_CHECKS.extend(SOFTMAX_CHECKS)

@@ -27,6 +27,13 @@ MUTATIONS = {
     "bf16_widen_shift": ("<< 16;", "<< 15;"),
     "sampled_row_index": ("(h * P.N + i) * P.d + c", "(h * P.N + r) * P.d + c"),
     "keys_as_queries": ("qrow[c] = widen(P.q,", "qrow[c] = widen(P.k,"),
+    "softmax_no_max": ("y[j] = std::exp(static_cast<double>(x[j]) - m);", "y[j] = std::exp(static_cast<double>(x[j]));"),
+    "softmax_no_normalisation": ("for (int64_t j = 0; j < C; ++j) y[j] /= l;", ""),
+    "softmax_dropped_first_term": ("    l += y[j];", "    if (j > 0) l += y[j];"),
+    "softmax_online_no_rescale": ("l = (l == 0.0 ? 0.0 : l * std::exp(m - m_new)) + cs;", "l = l + cs;"),
+    "softmax_online_rescale_sign": ("l * std::exp(m - m_new)", "l * std::exp(m_new - m)"),
+    "softmax_sampled_row_index": ("const float* row = x + (rows ? rows[i] : i) * C;\n      if (chunk == 0)",
+                                  "const float* row = x + i * C;\n      if (chunk == 0)"),
 }
 
 

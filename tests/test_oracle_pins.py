@@ -83,3 +83,8 @@ def test_bf16_widening_is_exact(orc):
 
 def test_golden_exact_rational(orc):
     C.check_golden_exact_rational(orc)
+
+
+@pytest.mark.parametrize("check", C.SOFTMAX_CHECKS, ids=lambda f: f.__name__[6:])
+def test_softmax_pins(orc, check):
+    check(orc)
