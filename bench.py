@@ -44,17 +44,24 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_digest() -> str:
-    """Digest of the HIP sources: counter figures are only valid for the kernel they were taken on.
+# The sources each operation's kernels and launch code are built from.
+OP_SOURCES = {
+    "attn": ("common.hpp", "api_util.hpp", "attn_bf16.hpp", "attn_f32.hpp", "hfa_api.hip"),
+    "softmax": ("common.hpp", "api_util.hpp", "softmax_rows.hpp", "softmax_api.hip"),
+}
+
+
+def kernel_source_digest(op: str = "attn") -> str:
+    """Digest of one operation's HIP sources: counter figures are only valid for the kernel they were taken on.
 
     Line comments and whitespace are dropped first, so editing prose does not void figures
     taken on the same code."""
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(ROOT, "fa2_fwd_amd", "csrc", "*"))):
-        with open(path, encoding="utf-8") as f:
+    for name in sorted(OP_SOURCES[op]):
+        with open(os.path.join(ROOT, "fa2_fwd_amd", "csrc", name), encoding="utf-8") as f:
             text = f.read()
         code = "".join(re.sub(r"//.*", "", line).strip() for line in text.splitlines())
-        h.update(os.path.basename(path).encode())
+        h.update(name.encode())
         h.update(re.sub(r"\s+", "", code).encode())
     return h.hexdigest()[:16]
 
@@ -147,6 +154,90 @@ def graph_time(w, count: int, reps: int):
         b.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b) / (reps * count)
+
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+
+
+def softmax_key(sw) -> str:
+    return f"softmax_rows_f32_{sw.rows}x{sw.cols}"
+
+
+def load_softmax_traffic(sw):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            entry = json.load(f).get(softmax_key(sw))
+    except (OSError, ValueError):
+        return None
+    if not entry or entry.get("src_digest") != kernel_source_digest("softmax"):
+        return None
+    return entry
+
+
+def time_softmax(sw, steps: int, warmup: int):
+    """hfa_softmax_rows on one resident fp32 matrix: ms per launch and algorithmic GB/s."""
+    import torch
+
+    import fa2_fwd_amd as hfa
+
+    x = sw.inputs().cuda()
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        hfa.softmax_rows(x, out=y, stream=stream)
+    torch.cuda.synchronize()
+    events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(steps):
+        events[i].record(stream)
+        hfa.softmax_rows(x, out=y, stream=stream)
+    events[steps].record(stream)
+    torch.cuda.synchronize()
+    ms = events[0].elapsed_time(events[steps]) / steps
+    per = sorted(events[i].elapsed_time(events[i + 1]) for i in range(steps))
+    gbs = sw.algorithmic_bytes / (ms * 1e-3) / 1e9
+    log(f"[bench] {sw.describe()}: {ms:.4f} ms/launch, {gbs:.0f} GB/s of algorithmic bytes, "
+        f"{100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak")
+    traffic = load_softmax_traffic(sw)
+    return {
+        "workload": sw.describe(),
+        "ms_per_step": round(ms, 5),
+        "ms_median": round(per[len(per) // 2], 5),
+        "ms_min": round(per[0], 5),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": None if traffic is None else int(traffic["hbm_bytes_per_launch"]),
+            "algorithmic_bytes": sw.algorithmic_bytes,
+            "kernel": softmax_key(sw),
+        },
+    }
+
+
+def softmax_cpu_baseline(sw, target_s: float):
+    """The fp64 oracle on an evenly spaced sample of rows, in algorithmic GB/s."""
+    import numpy as np
+
+    import oracle
+
+    x = sw.inputs().numpy()
+    threads = oracle.default_threads()
+
+    def run(n):
+        rows = np.linspace(0, sw.rows - 1, n).round().astype(np.int64)
+        t0 = time.perf_counter()
+        oracle.softmax_rows(x, rows=rows, threads=threads)
+        return time.perf_counter() - t0
+
+    t1 = run(min(sw.rows, 16))
+    n = int(min(sw.rows, max(16, round(16 * target_s / max(t1, 1e-6)))))
+    t = run(n)
+    gbs = 2 * n * sw.cols * 4 / t / 1e9
+    log(f"[bench] oracle softmax: {n} rows in {t:.2f} s on {threads} threads -> {gbs:.2f} GB/s")
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} of {sw.rows} rows (evenly spaced), fp64 definition; {t:.2f} s"}
 
 
 def _sclk_files():
@@ -247,6 +338,23 @@ def cpu_baseline(w, target_s: float):
     }
 
 
+def profile_pass_softmax(sw, launches: int) -> None:
+    """A few softmax launches and one device copy of COPY_BYTES, for counter runs."""
+    import torch
+
+    import fa2_fwd_amd as hfa
+
+    x = sw.inputs().cuda()
+    for _ in range(launches):
+        hfa.softmax_rows(x)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=x.device)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[profile] {launches} launches of {sw.describe()} and one {COPY_BYTES} B copy done")
+
+
 def profile_pass(w, launches: int) -> None:
     """A few kernel launches and one device copy of COPY_BYTES, for counter runs."""
     import torch
@@ -280,43 +388,47 @@ def _read_counter(dirpath: str, counter: str):
     return out
 
 
-def summarize_pmc(w, fetch_dir: str, write_dir: str) -> None:
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the attention kernel, each scaled
-    by what the same counter reads for the copy of known size."""
+def summarize_pmc(w, fetch_dir: str, write_dir: str, op: str = "attn") -> None:
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the measured kernel (attention, or the
+    row softmax when op == "softmax"), each scaled by what the same counter reads for the
+    copy of known size."""
+    marker = "attn_fwd" if op == "attn" else "softmax_rows"
     result = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _read_counter(d, counter)
-        attn = [v for name, v in rows if "attn_fwd" in name]
+        kern = [v for name, v in rows if marker in name]
         # The device-to-device copy is HIP's blit kernel; fall back to the
-        # largest non-attention dispatch if the runtime names it differently.
+        # largest other dispatch if the runtime names it differently.
         copies = [v for name, v in rows if "copyBuffer" in name]
         if not copies:
-            copies = [v for name, v in rows if "attn_fwd" not in name and v * 1024 > COPY_BYTES * 0.25]
-        if not attn or not copies:
-            raise RuntimeError(f"{counter}: missing attention ({len(attn)}) or copy ({len(copies)}) dispatches")
+            copies = [v for name, v in rows if marker not in name and v * 1024 > COPY_BYTES * 0.25]
+        if not kern or not copies:
+            raise RuntimeError(f"{counter}: missing {marker} ({len(kern)}) or copy ({len(copies)}) dispatches")
         copy_kib = max(copies)
         factor = (COPY_BYTES / 1024) / copy_kib
-        attn_kib = sum(attn) / len(attn)
-        result[counter] = {"attn_kib_per_dispatch": attn_kib, "copy_kib": copy_kib, "scale": factor,
-                           "bytes_per_launch": attn_kib * 1024 * factor}
+        kib = sum(kern) / len(kern)
+        result[counter] = {"kernel_kib_per_dispatch": kib, "copy_kib": copy_kib, "scale": factor,
+                           "bytes_per_launch": kib * 1024 * factor}
     table = {}
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             table = json.load(f)
     total = result["FETCH_SIZE"]["bytes_per_launch"] + result["WRITE_SIZE"]["bytes_per_launch"]
-    table[kernel_key(w) + f"_N{w.N}"] = {
+    key = kernel_key(w) + f"_N{w.N}" if op == "attn" else softmax_key(w)
+    alg = algorithmic_bytes(w) if op == "attn" else w.algorithmic_bytes
+    table[key] = {
         "workload": w.describe(),
-        "src_digest": kernel_source_digest(),
+        "src_digest": kernel_source_digest(op),
         "fetch": result["FETCH_SIZE"],
         "write": result["WRITE_SIZE"],
         "hbm_bytes_per_launch": total,
-        "algorithmic_bytes": algorithmic_bytes(w),
+        "algorithmic_bytes": alg,
     }
     os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(table, f, indent=2, sort_keys=True)
         f.write("\n")
-    log(f"[pmc] {w.describe()}: HBM {total / 1e6:.1f} MB/launch vs algorithmic {algorithmic_bytes(w) / 1e6:.1f} MB")
+    log(f"[pmc] {w.describe()}: HBM {total / 1e6:.1f} MB/launch vs algorithmic {alg / 1e6:.1f} MB")
 
 
 def main() -> int:
@@ -333,10 +445,21 @@ def main() -> int:
     ap.add_argument("--profile-pass", action="store_true")
     ap.add_argument("--launches", type=int, default=3)
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--op", choices=("attn", "softmax"), default="attn",
+                    help="kernel for --profile-pass / --summarize-pmc / --softmax-only (softmax: --config 1 or 2)")
+    ap.add_argument("--softmax-only", action="store_true", help="time only the row softmax workload --config")
+    ap.add_argument("--no-softmax", action="store_true", help="skip the row softmax workloads")
     args = ap.parse_args()
 
     from fa2_fwd_amd import workloads as W
 
+    if args.op == "softmax" and (args.summarize_pmc or args.profile_pass):
+        sw = W.SOFTMAX_CONFIGS[args.config]
+        if args.summarize_pmc:
+            summarize_pmc(sw, *args.summarize_pmc, op="softmax")
+        else:
+            profile_pass_softmax(sw, args.launches)
+        return 0
     w = W.CONFIGS[args.config]
     if args.summarize_pmc:
         summarize_pmc(w, *args.summarize_pmc)
@@ -354,6 +477,9 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    if args.softmax_only:
+        print(json.dumps(time_softmax(W.SOFTMAX_CONFIGS[args.config], args.steps, args.warmup)), flush=True)
+        return 0
     main_res = time_gpu(w, args.steps, args.warmup)
     secondary = None
     if args.secondary and args.secondary != args.config:
@@ -392,6 +518,15 @@ def main() -> int:
     sclk = None if args.no_sclk else observed_sclk(w, 0.5)
     if sclk is not None:
         log(f"[bench] shader clock during {w.describe()}: {sclk:.0f} MHz (median of sysfs samples)")
+    softmax = None
+    if not args.no_softmax:
+        softmax = []
+        for n, sw in sorted(W.SOFTMAX_CONFIGS.items()):
+            entry = time_softmax(sw, args.steps, args.warmup)
+            entry["config"] = n
+            if n == 1 and not args.no_cpu_baseline:
+                entry["cpu_baseline"] = softmax_cpu_baseline(sw, 3.0)
+            softmax.append(entry)
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
     props = torch.cuda.get_device_properties(0)
     line = {
@@ -414,6 +549,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "secondary": secondary,
         "all_configs": all_configs,
+        "softmax_rows": softmax,
         "observed_sclk_mhz": sclk,
         "device": getattr(props, "gcnArchName", props.name),
     }

@@ -31,7 +31,7 @@ HFA_ERR_NO_DEVICE = 7
 HFA_ERR_LAUNCH = 8
 
 EXPORTED = ("hfa_attn_fwd", "hfa_status_str", "hfa_block_rows", "hfa_attn_fwd_graph_create", "hfa_graph_launch",
-            "hfa_graph_destroy")
+            "hfa_graph_destroy", "hfa_softmax_rows")
 
 _lib = None
 
@@ -71,6 +71,8 @@ def load_library(path: str | Path | None = None) -> ctypes.CDLL:
     lib.hfa_graph_launch.restype = ctypes.c_int
     lib.hfa_graph_destroy.argtypes = [vp]
     lib.hfa_graph_destroy.restype = None
+    lib.hfa_softmax_rows.argtypes = [vp, vp, i64, i64, vp]
+    lib.hfa_softmax_rows.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -103,6 +105,30 @@ def hfa_graph_launch(graph, stream) -> int:
 
 def hfa_graph_destroy(graph) -> None:
     load_library().hfa_graph_destroy(graph)
+
+
+def hfa_softmax_rows(x, y, rows, cols, stream) -> int:
+    """Raw C-ABI call: pointers as ints (device addresses) or None; returns the status."""
+    return load_library().hfa_softmax_rows(x, y, rows, cols, stream)
+
+
+def softmax_rows(x, out=None, stream=None):
+    """Row softmax of a contiguous float32 [rows, cols] device tensor (``out`` may be ``x``)."""
+    import torch
+
+    if not isinstance(x, torch.Tensor) or x.ndim != 2 or x.dtype != torch.float32:
+        raise ValueError("softmax_rows needs a float32 [rows, cols] tensor")
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError("softmax_rows needs a contiguous GPU tensor")
+    if out is None:
+        out = torch.empty_like(x)
+    elif out.shape != x.shape or out.dtype != x.dtype or out.device != x.device or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor like x")
+    with torch.cuda.device(x.device):
+        st = hfa_softmax_rows(x.data_ptr(), out.data_ptr(), x.shape[0], x.shape[1], _stream_handle(stream, x.device))
+    if st != HFA_OK:
+        raise HfaError(st)
+    return out
 
 
 def _dtype_code(t) -> int:

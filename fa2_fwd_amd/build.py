@@ -1,7 +1,7 @@
 """Builds ``libhfa.so`` (the gfx950 attention library) in-tree with hipcc.
 
-The library is one translation unit, ``csrc/hfa_api.hip``, compiled for
-gfx950 only.  Packed-fp32 VALU instructions are disabled for all device code.
+The library is built from every ``csrc/*.hip`` translation unit (one per
+operation: attention, row softmax, ...), compiled for gfx950 only.  Packed-fp32 VALU instructions are disabled for all device code.
 """
 
 from __future__ import annotations
@@ -13,7 +13,7 @@ from pathlib import Path
 PKG = Path(__file__).resolve().parent
 ROOT = PKG.parent
 LIB_PATH = PKG / "libhfa.so"
-SOURCES = [PKG / "csrc" / "hfa_api.hip"]
+SOURCES = sorted((PKG / "csrc").glob("*.hip"))
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

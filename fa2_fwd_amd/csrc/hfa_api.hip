@@ -1,22 +1,22 @@
-// C ABI of libhfa.so (declared in include/hfa.h): argument validation, device
-// check and kernel dispatch for the gfx950 attention forward.
+// C ABI of the attention forward in libhfa.so (declared in include/hfa.h):
+// argument validation, device check, kernel dispatch and graph capture.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdint>
-#include <cstring>
 #include <mutex>
 #include <new>
 
 #include "hfa.h"
 #include "attn_bf16.hpp"
 #include "attn_f32.hpp"
+#include "api_util.hpp"
 
 namespace {
 
 using namespace hfa;
+using namespace hfa::api;
 
 // Tile configurations, one per (dtype, head dim).  The macros exist so that
 // a tile sweep can build variants with -D; the defaults are the tuned choice.
@@ -52,35 +52,6 @@ constexpr int64_t kComputeUnits = 256;  // gfx950 (MI350 series): 8 XCDs x 32 CU
 bool f32_d64_big(int64_t BH, int64_t N) {
   const int64_t wgs = BH * ((N + F32D64Big::BR - 1) / F32D64Big::BR);
   return wgs >= kComputeUnits;
-}
-
-bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
-  const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
-  return pa < pb + nb && pb < pa + na;
-}
-
-// Whether the current device is a gfx950; cached per device ordinal.
-constexpr int kMaxDevices = 64;
-std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
-
-hfa_status check_device() {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
-    (void)hipGetLastError();
-    return HFA_ERR_NO_DEVICE;
-  }
-  if (dev >= kMaxDevices) return HFA_ERR_NO_DEVICE;
-  int st = g_arch_state[dev].load(std::memory_order_acquire);
-  if (st == 0) {
-    hipDeviceProp_t prop;
-    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
-      (void)hipGetLastError();
-      return HFA_ERR_NO_DEVICE;
-    }
-    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
-    g_arch_state[dev].store(st, std::memory_order_release);
-  }
-  return st == 1 ? HFA_OK : HFA_ERR_NO_DEVICE;
 }
 
 // Raise the dynamic-LDS limit of a kernel once per process (per device the
@@ -159,7 +130,6 @@ hfa_status validate(const void* q, const void* k, const void* v, const void* o, 
   const int64_t BH = B * H;
   if (BH > INT_MAX) return HFA_ERR_SHAPE;
   if (!std::isfinite(scale)) return HFA_ERR_SCALE;
-  auto misaligned = [](const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) != 0; };
   if (misaligned(q, 16) || misaligned(k, 16) || misaligned(v, 16) || misaligned(o, 16) || misaligned(lse, 4))
     return HFA_ERR_ALIGN;
   const size_t elt = dtype == HFA_F32 ? 4 : 2;

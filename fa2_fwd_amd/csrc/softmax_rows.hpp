@@ -1,0 +1,170 @@
+// Row softmax of an fp32 matrix for gfx950: y[r, :] = softmax(x[r, :]).
+//
+// The stable row softmax of the book chapter "Triton and kernel fusion"
+// (section "Fusion": subtract the row max, exponentiate, sum, divide; one read
+// of x and one write of y instead of about eight passes), extended to rows
+// wider than what one block holds by the route its stretch exercise names: a
+// running max and a running sum (the online normalisation identity of
+// neuralmasteryai "Hardware Acceleration & Custom Kernels", section 2, step 2).
+//
+// One workgroup per row.  Every thread folds its elements into a pair (m, l)
+// = (max, sum of exp(x - m)); pairs are merged by the same identity,
+//     (m, l) + (m', l') = (M, l e^(m - M) + l' e^(m' - M)),  M = max(m, m'),
+// first across the 64 lanes of a wave, then across the waves through LDS.
+//
+//  * Resident path (cols <= NT * 4 * ITEMS): the thread's elements stay in
+//    registers between the reduction and the output: x is read once.
+//  * Streaming path: the thread's running pair is updated chunk by chunk
+//    while x streams through (UNROLL 16-byte loads in flight per thread), then
+//    x is read a second time to write y.
+//
+// Exponentials are exp2 of (x - M) * log2(e), the difference taken first so
+// that large |x| loses no accuracy.  Element i of a row is read and written by
+// the same thread, and every read precedes the reduction barrier, so y may be
+// x itself.
+#pragma once
+
+#include "common.hpp"
+
+namespace hfa {
+
+constexpr float kLog2eF = 1.44269504088896340736f;
+
+struct SoftmaxPair {
+  float m, l;  // running max and running sum of exp(x - m)
+};
+
+// The merge identity.  An empty pair (-inf, 0) is neutral; the weights of the
+// two sides are formed only for a finite joint max.
+__device__ __forceinline__ SoftmaxPair merge_pairs(SoftmaxPair a, SoftmaxPair b) {
+  const float M = fmaxf(a.m, b.m);
+  if (M == -INFINITY) return {M, 0.0f};
+  const float wa = a.m == -INFINITY ? 0.0f : exp2_hw((a.m - M) * kLog2eF);
+  const float wb = b.m == -INFINITY ? 0.0f : exp2_hw((b.m - M) * kLog2eF);
+  return {M, a.l * wa + b.l * wb};
+}
+
+// Fold n values (-inf marks an absent one) into a running pair.
+template <int NV>
+__device__ __forceinline__ SoftmaxPair fold_values(SoftmaxPair p, const float (&v)[NV]) {
+  float cm = v[0];
+#pragma unroll
+  for (int i = 1; i < NV; ++i) cm = fmaxf(cm, v[i]);
+  const float M = fmaxf(p.m, cm);
+  if (M == -INFINITY) return p;
+  float s = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) s += v[i] == -INFINITY ? 0.0f : exp2_hw((v[i] - M) * kLog2eF);
+  const float w = p.m == -INFINITY ? 0.0f : exp2_hw((p.m - M) * kLog2eF);
+  return {M, p.l * w + s};
+}
+
+// Merge the pairs of all threads of the workgroup; every thread gets the total.
+template <int NT>
+__device__ __forceinline__ SoftmaxPair merge_workgroup(SoftmaxPair p, SoftmaxPair* lds) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const SoftmaxPair o = {__shfl_xor(p.m, off), __shfl_xor(p.l, off)};
+    p = merge_pairs(p, o);
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) lds[wave] = p;
+  __syncthreads();
+  SoftmaxPair t = lds[0];
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w) t = merge_pairs(t, lds[w]);
+  return t;
+}
+
+// Element e (0..3) of slot s of thread tid: 16-byte vectors when VEC (row
+// width a multiple of 4 and 16-byte aligned rows), else a coalesced scalar
+// layout.
+template <int NT, bool VEC>
+__device__ __forceinline__ int64_t slot_index(int64_t base, int s, int tid, int e) {
+  return VEC ? base + (static_cast<int64_t>(s) * NT + tid) * 4 + e : base + (static_cast<int64_t>(s) * 4 + e) * NT + tid;
+}
+
+template <int NT, bool VEC, int SLOTS>
+__device__ __forceinline__ void load_slots(const float* xr, int64_t base, int64_t cols, int tid, float (&v)[SLOTS * 4]) {
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    if (VEC) {
+      const int64_t i0 = slot_index<NT, true>(base, s, tid, 0);
+      if (i0 < cols) {
+        const f32x4 q = *reinterpret_cast<const f32x4*>(xr + i0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * s + e] = q[e];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * s + e] = -INFINITY;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t i = slot_index<NT, false>(base, s, tid, e);
+        v[4 * s + e] = i < cols ? xr[i] : -INFINITY;
+      }
+    }
+  }
+}
+
+template <int NT, bool VEC, int SLOTS>
+__device__ __forceinline__ void store_slots(float* yr, int64_t base, int64_t cols, int tid, const float (&v)[SLOTS * 4],
+                                            float M, float inv) {
+#pragma unroll
+  for (int s = 0; s < SLOTS; ++s) {
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = exp2_hw((v[4 * s + e] - M) * kLog2eF) * inv;
+    if (VEC) {
+      const int64_t i0 = slot_index<NT, true>(base, s, tid, 0);
+      if (i0 < cols) *reinterpret_cast<f32x4*>(yr + i0) = f32x4{o[0], o[1], o[2], o[3]};
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t i = slot_index<NT, false>(base, s, tid, e);
+        if (i < cols) yr[i] = o[e];
+      }
+    }
+  }
+}
+
+// Resident path: the row's NT * 4 * ITEMS slots stay in registers.
+template <int NT, int ITEMS, bool VEC>
+__global__ __launch_bounds__(NT) void softmax_rows_resident_kernel(const float* x, float* y, int64_t cols) {
+  __shared__ SoftmaxPair lds[NT / 64];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const float* xr = x + row * cols;
+  float* yr = y + row * cols;
+  float v[ITEMS * 4];
+  load_slots<NT, VEC, ITEMS>(xr, 0, cols, tid, v);
+  const SoftmaxPair p = merge_workgroup<NT>(fold_values(SoftmaxPair{-INFINITY, 0.0f}, v), lds);
+  store_slots<NT, VEC, ITEMS>(yr, 0, cols, tid, v, p.m, 1.0f / p.l);
+}
+
+// Streaming path: x read twice, UNROLL slots per thread in flight.
+template <int NT, int UNROLL, bool VEC>
+__global__ __launch_bounds__(NT) void softmax_rows_stream_kernel(const float* x, float* y, int64_t cols) {
+  __shared__ SoftmaxPair lds[NT / 64];
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const float* xr = x + row * cols;
+  float* yr = y + row * cols;
+  constexpr int64_t STEP = static_cast<int64_t>(NT) * 4 * UNROLL;
+  SoftmaxPair p = {-INFINITY, 0.0f};
+  for (int64_t base = 0; base < cols; base += STEP) {
+    float v[UNROLL * 4];
+    load_slots<NT, VEC, UNROLL>(xr, base, cols, tid, v);
+    p = fold_values(p, v);
+  }
+  p = merge_workgroup<NT>(p, lds);
+  const float inv = 1.0f / p.l;
+  for (int64_t base = 0; base < cols; base += STEP) {
+    float v[UNROLL * 4];
+    load_slots<NT, VEC, UNROLL>(xr, base, cols, tid, v);
+    store_slots<NT, VEC, UNROLL>(yr, base, cols, tid, v, p.m, inv);
+  }
+}
+
+}  // namespace hfa

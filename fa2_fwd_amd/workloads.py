@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the attention forward.
+"""Seeded synthetic inputs for the attention forward and the row softmax.
 
 This module only draws random numbers and lays them out; it holds none of the
 attention arithmetic, so both the GPU path's tests and the CPU oracle can take
@@ -55,6 +55,38 @@ CONFIGS = {
     3: Workload("cfg3", 4, 8, 2048, 64, "f32", 3, qk_mult=4.0),
     4: Workload("cfg4", 2, 32, 4096, 128, "bf16", 4),
     5: Workload("cfg5", 1, 16, 16384, 128, "bf16", 5),
+}
+
+
+@dataclass(frozen=True)
+class SoftmaxWorkload:
+    """Row softmax of a seeded N(0, scale^2) fp32 [rows, cols] matrix."""
+
+    name: str
+    rows: int
+    cols: int
+    seed: int
+    scale: float = 4.0
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """The method's minimum traffic: read x once, write y once (fp32)."""
+        return 2 * self.rows * self.cols * 4
+
+    def describe(self) -> str:
+        return f"softmax_rows {self.rows}x{self.cols} f32 seed={self.seed}"
+
+    def inputs(self) -> torch.Tensor:
+        g = torch.Generator("cpu").manual_seed(int(self.seed))
+        return (torch.randn(self.rows, self.cols, generator=g, dtype=torch.float32) * self.scale).contiguous()
+
+
+# Row softmax workloads: the [4096, 32000] fp32 matrix of the book chapter
+# "Triton and kernel fusion" (section "Fusion"), and rows four times wider
+# than that chapter's one-block limit of 65536 columns.
+SOFTMAX_CONFIGS = {
+    1: SoftmaxWorkload("softmax1", 4096, 32000, 101),
+    2: SoftmaxWorkload("softmax2", 256, 262144, 102),
 }
 
 

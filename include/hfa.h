@@ -121,6 +121,30 @@ hfa_status hfa_graph_launch(hfa_graph g, void* stream);
  * synchronise its streams first. */
 void hfa_graph_destroy(hfa_graph g);
 
+/* Row softmax of an fp32 matrix: y[r, :] = exp(x[r, :] - m_r) / sum_j
+ * exp(x[r, j] - m_r), m_r = max_j x[r, j].
+ *
+ * The stable row softmax of the book chapter "Triton and kernel fusion"
+ * (section "Fusion": one read of x and one write of y), for any row width:
+ * rows wider than one workgroup holds in registers (more than 32768 columns)
+ * take the route of that chapter's stretch exercise, a running max and running
+ * sum per thread (the online normalisation identity of neuralmasteryai
+ * "Hardware Acceleration & Custom Kernels", section 2, step 2), and read x a
+ * second time to write y.  Arithmetic is fp32 with hardware exp2.
+ *
+ *   x, y        device, [rows, cols] contiguous fp32, 4-byte aligned (16-byte
+ *               alignment with cols % 4 == 0 takes 16-byte accesses).  y may
+ *               be x itself (in place) but must not partly overlap it.
+ *   rows, cols  >= 1, rows < 2^31, rows * cols * 4 bytes addressable.
+ *   stream      a hipStream_t, passed as a pointer; NULL selects the null stream.
+ *
+ * Finite inputs give finite outputs; -inf entries get weight 0, NaN and +inf
+ * propagate.  Validation precedes any HIP call: HFA_ERR_NULL, HFA_ERR_SHAPE,
+ * HFA_ERR_ALIGN, HFA_ERR_ALIAS (partial overlap), HFA_ERR_NO_DEVICE, then
+ * HFA_ERR_LAUNCH if the launch fails.  Asynchronous on `stream`; allocates
+ * nothing. */
+hfa_status hfa_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

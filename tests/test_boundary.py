@@ -173,3 +173,20 @@ def test_graph_null_handles():
     import ctypes
     assert lib.hfa_attn_fwd_graph_create(0x100000, 0x200000, 0x300000, 0x400000, 0x500000, 1, 1, 128, 64,
                                          0.125, hfa.HFA_F32, 1, None) == hfa.HFA_ERR_NULL
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), hfa.HFA_ERR_NULL),
+    (dict(y=None), hfa.HFA_ERR_NULL),
+    (dict(rows=0), hfa.HFA_ERR_SHAPE),
+    (dict(cols=0), hfa.HFA_ERR_SHAPE),
+    (dict(rows=1 << 31), hfa.HFA_ERR_SHAPE),
+    (dict(rows=1 << 30, cols=1 << 33), hfa.HFA_ERR_SHAPE),
+    (dict(x=0x100002), hfa.HFA_ERR_ALIGN),
+    (dict(y=0x900001), hfa.HFA_ERR_ALIGN),
+    (dict(y=0x100000 + 64), hfa.HFA_ERR_ALIAS),
+])
+def test_softmax_rows_rejects_before_any_hip_call(kw, status):
+    a = dict(x=0x100000, y=0x900000, rows=4, cols=1000, stream=None)
+    a.update(kw)
+    assert hfa.hfa_softmax_rows(a["x"], a["y"], a["rows"], a["cols"], a["stream"]) == status

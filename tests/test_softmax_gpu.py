@@ -1,0 +1,96 @@
+"""GPU parity of hfa_softmax_rows against the fp64 CPU oracle.
+
+Tolerance: max |gpu - oracle| <= 1e-5 per element (the fp32 bound used for
+attention; softmax outputs lie in [0, 1]).  Shapes cover the book chapter's
+[4096, 32000] matrix, rows wider than its one-block limit (65536, the
+streaming path), widths that are not multiples of 4 and misaligned rows (the
+scalar path), tiny widths, in-place use, inputs near the exp overflow range and
+-inf entries.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fa2_fwd_amd as hfa
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+ATOL = 1e-5
+
+
+def _x(rows, cols, seed, scale=4.0, shift=0.0):
+    g = torch.Generator("cpu").manual_seed(seed)
+    return (torch.randn(rows, cols, generator=g) * scale + shift).contiguous()
+
+
+def _check(name, x_host, y_dev, rows=None):
+    print(f"[softmax] {name}", flush=True)
+    y = y_dev.cpu().double().numpy()
+    ref = oracle.softmax_rows(x_host.numpy(), rows=rows)
+    if rows is not None:
+        y = y[rows]
+    assert np.isfinite(y).all(), f"{name}: non-finite output"
+    err = np.abs(y - ref).max()
+    print(f"[softmax] {name}: max|d|={err:.3e}", flush=True)
+    assert err <= ATOL, f"{name}: off by {err:.3e}"
+
+
+@pytest.mark.parametrize("rows,cols", [(4096, 32000), (64, 70001), (8, 262144), (8, 262147), (3, 32768),
+                                       (5, 32769), (7, 1000), (9, 1001), (2, 1), (3, 3), (1, 5)])
+def test_softmax_rows_shapes(rows, cols):
+    x = _x(rows, cols, seed=rows * 7 + cols)
+    y = hfa.softmax_rows(x.cuda())
+    torch.cuda.synchronize()
+    sample = None if rows * cols <= 4_000_000 else np.unique(np.r_[0, 1, rows // 2, rows - 1,
+                                                             np.random.default_rng(cols).integers(0, rows, 24)])
+    _check(f"{rows}x{cols}", x, y, rows=sample)
+
+
+def test_softmax_rows_in_place():
+    x = _x(16, 5000, seed=3)
+    xd = x.cuda()
+    y = hfa.softmax_rows(xd, out=xd)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == xd.data_ptr()
+    _check("in place", x, xd)
+
+
+def test_softmax_rows_misaligned_rows():
+    # a view starting one float into the buffer: 4-byte aligned only
+    x = _x(6, 4000, seed=5)
+    buf = torch.empty(6 * 4000 + 1, device="cuda")
+    xd = buf[1:].view(6, 4000)
+    xd.copy_(x.cuda())
+    y = hfa.softmax_rows(xd)
+    torch.cuda.synchronize()
+    _check("misaligned", x, y)
+
+
+def test_softmax_rows_large_magnitudes():
+    x = _x(4, 40000, seed=6, scale=30.0, shift=750.0)
+    y = hfa.softmax_rows(x.cuda())
+    torch.cuda.synchronize()
+    _check("near exp overflow", x, y)
+
+
+def test_softmax_rows_minus_inf_entries():
+    x = _x(3, 2000, seed=8)
+    x[:, ::7] = -float("inf")
+    y = hfa.softmax_rows(x.cuda()).cpu().double().numpy()
+    finite = x.clone()
+    keep = ~torch.isinf(x)
+    ref = np.zeros((3, 2000))
+    for r in range(3):
+        cols = keep[r].numpy()
+        ref[r, cols] = oracle.softmax_rows(finite[r:r + 1, cols].contiguous().numpy())[0]
+    assert np.all(y[:, ::7] == 0.0)
+    assert np.abs(y - ref).max() <= ATOL
+
+
+def test_softmax_rows_rows_sum_to_one_on_device():
+    x = _x(256, 100000, seed=9, scale=10.0)
+    y = hfa.softmax_rows(x.cuda())
+    s = y.double().sum(dim=1)
+    assert torch.all((s - 1).abs() < 1e-4)
