@@ -22,7 +22,12 @@ identity of that section 2, step 2, tile by tile over the keys.
 ``softmax_rows_online`` takes the row max and sum in one sweep by the same
 running identity, over chunks of any width.
 
-Inputs are numpy arrays of shape [B, H, N, d]: ``float32`` for fp32 data, or
+``rmsnorm`` is the RMS normalisation of the TritonForge "Fused RMSNorm" card,
+y = x / sqrt(sum_i x_i^2 / d + eps) * w per row, with the optional residual
+of that chapter's "Fused residual add + RMSNorm" section added first (in fp32,
+as the chapter's kernel adds it); it returns y and the sum.
+
+Attention inputs are numpy arrays of shape [B, H, N, d]: ``float32`` for fp32 data, or
 ``uint16`` holding bf16 bit patterns.  Outputs are fp64.
 """
 
@@ -82,6 +87,9 @@ class OracleLib:
         lib.hfa_ref_softmax_rows.restype = ctypes.c_int
         lib.hfa_ref_softmax_rows_online.argtypes = [vp, i64, i64, i64, vp, i64, vp, ctypes.c_int]
         lib.hfa_ref_softmax_rows_online.restype = ctypes.c_int
+        lib.hfa_ref_rmsnorm.argtypes = [vp, vp, vp, ctypes.c_int, i64, i64, ctypes.c_double, vp, i64, vp, vp,
+                                        ctypes.c_int]
+        lib.hfa_ref_rmsnorm.restype = ctypes.c_int
         self.lib = lib
         self.path = str(path)
 
@@ -135,6 +143,41 @@ class OracleLib:
         """Row softmax with (max, sum) taken by the running identity over chunks of ``chunk`` columns."""
         return self._softmax(x, rows, threads, chunk=chunk)
 
+    def rmsnorm(self, x, weight, eps, residual=None, rows=None, threads=0):
+        """RMS normalisation of the rows of x [R, C] (float32, or uint16 bf16 patterns) in fp64.
+
+        Returns (y, s): y = s / sqrt(mean_j s_j^2 + eps) * weight and s = x + residual formed in
+        fp32 (s = x without a residual), both fp64 [R or len(rows), C]."""
+        x = np.ascontiguousarray(x)
+        w = np.ascontiguousarray(weight)
+        if x.ndim != 2 or w.ndim != 1 or w.shape[0] != x.shape[1]:
+            raise ValueError("rmsnorm oracle takes x [R, C] and weight [C]")
+        if x.dtype == np.float32:
+            code = 0
+        elif x.dtype == np.uint16:
+            code = 1
+        else:
+            raise ValueError("oracle inputs are float32 or uint16 (bf16 bit patterns), got %s" % x.dtype)
+        if w.dtype != x.dtype:
+            raise ValueError("weight must have x's dtype")
+        r = None
+        if residual is not None:
+            r = np.ascontiguousarray(residual)
+            if r.shape != x.shape or r.dtype != x.dtype:
+                raise ValueError("residual must match x")
+        R, C = x.shape
+        rows_arr = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        n = R if rows_arr is None else rows_arr.shape[0]
+        y = np.empty((n, C), dtype=np.float64)
+        s = np.empty((n, C), dtype=np.float64)
+        thr = int(threads) if threads else default_threads()
+        rc = self.lib.hfa_ref_rmsnorm(x.ctypes.data, None if r is None else r.ctypes.data, w.ctypes.data, code, R, C,
+                                      float(eps), None if rows_arr is None else rows_arr.ctypes.data,
+                                      n if rows_arr is not None else 0, y.ctypes.data, s.ctypes.data, thr)
+        if rc != 0:
+            raise ValueError("oracle rejected its arguments (rmsnorm)")
+        return y, s
+
     def attn_fwd(self, q, k, v, scale, rows=None, threads=0):
         """Definition-form attention forward in fp64.  Returns (O [B,H,R,d], LSE [B,H,R])."""
         return self._call("hfa_ref_attn_fwd", q, k, v, scale, rows, threads)
@@ -177,3 +220,8 @@ def softmax_rows(x, rows=None, threads=0):
 def softmax_rows_online(x, chunk, rows=None, threads=0):
     """Row softmax in fp64 with (max, sum) by the running identity over chunks of ``chunk`` columns."""
     return default().softmax_rows_online(x, chunk, rows, threads)
+
+
+def rmsnorm(x, weight, eps, residual=None, rows=None, threads=0):
+    """RMS normalisation in fp64 of x [R, C] (+ residual, added in fp32).  Returns (y, s)."""
+    return default().rmsnorm(x, weight, eps, residual, rows, threads)

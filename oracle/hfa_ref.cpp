@@ -43,6 +43,18 @@
 //                               the scalar recurrence.  Used only to pin the
 //                               identity against the definition.
 //
+// One more for the RMS normalisation of the same pages (TritonForge "Fused
+// RMSNorm" card: RMSNorm(x) = x / sqrt(sum_i x_i^2 / d + eps) * gamma; book
+// chapter "Triton and kernel fusion", section "Fused residual add + RMSNorm":
+// the residual is added first, the sum is normalised, and the sum itself is
+// returned as a second output):
+//
+//  hfa_ref_rmsnorm  s_ij = x_ij + r_ij, formed in fp32 as the chapter's kernel
+//                   forms it (both operands upcast to fp32, one fp32 add; s = x
+//                   when there is no residual), then in fp64
+//                   y_ij = s_ij / sqrt(sum_j s_ij^2 / C + eps) * w_j.
+//                   Returns y and s, both fp64.
+//
 // Both attention entry points also return the row log-sum-exp
 // LSE_i = ln(sum_j exp(s_ij)) of the scaled scores (natural log).  The pages do not define it; it is the plain
 // reading: the running max plus the log of the running denominator.
@@ -271,9 +283,86 @@ int softmax_check_and_run(const float* x, int64_t R, int64_t C, int64_t chunk, c
   return 0;
 }
 
+// ---- RMS normalisation ---------------------------------------------------------
+
+// The fp32 sum of the chapter's kernel: both operands upcast to fp32, one
+// IEEE fp32 add (round to nearest even; the build disables contraction).
+double residual_sum(const void* x, const void* r, int dtype, int64_t idx) {
+  const float a = static_cast<float>(widen(x, dtype, idx));
+  if (!r) return static_cast<double>(a);
+  const float b = static_cast<float>(widen(r, dtype, idx));
+  const float sum = a + b;
+  return static_cast<double>(sum);
+}
+
+// One row: the sum, its mean square, the normalised and weighted output.
+// Returns false when the mean square plus eps is not positive.
+bool rmsnorm_row(const void* x, const void* r, const void* w, int dtype, int64_t row, int64_t C,
+                 double eps, double* y, double* s) {
+  double sq = 0.0;
+  for (int64_t j = 0; j < C; ++j) {
+    s[j] = residual_sum(x, r, dtype, row * C + j);
+    sq += s[j] * s[j];
+  }
+  const double denom = std::sqrt(sq / static_cast<double>(C) + eps);
+  if (!(denom > 0.0)) return false;
+  for (int64_t j = 0; j < C; ++j) y[j] = s[j] / denom * widen(w, dtype, j);
+  return true;
+}
+
+int rmsnorm_check_and_run(const void* x, const void* r, const void* w, int dtype, int64_t R, int64_t C,
+                          double eps, const int64_t* rows, int64_t n_rows, double* y, double* s_out,
+                          int threads) {
+  if (!x || !w || !y || R < 1 || C < 1 || (dtype != 0 && dtype != 1)) return -1;
+  if (!std::isfinite(eps) || eps < 0.0) return -1;
+  const int64_t n = rows ? n_rows : R;
+  if (n < 0) return -1;
+  if (rows)
+    for (int64_t i = 0; i < n_rows; ++i)
+      if (rows[i] < 0 || rows[i] >= R) return -1;
+  for (int64_t j = 0; j < C; ++j)
+    if (!std::isfinite(widen(w, dtype, j))) return -1;
+  for (int64_t i = 0; i < n; ++i) {
+    const int64_t row = rows ? rows[i] : i;
+    for (int64_t j = 0; j < C; ++j) {
+      if (!std::isfinite(widen(x, dtype, row * C + j))) return -1;
+      if (r && !std::isfinite(widen(r, dtype, row * C + j))) return -1;
+    }
+  }
+  if (threads < 1) threads = static_cast<int>(std::max(1u, std::thread::hardware_concurrency()));
+  std::vector<int> ok(static_cast<size_t>(threads), 1);
+  auto worker = [&](int t, int64_t b, int64_t e) {
+    std::vector<double> scratch(static_cast<size_t>(C));
+    for (int64_t i = b; i < e; ++i) {
+      double* s = s_out ? s_out + i * C : scratch.data();
+      if (!rmsnorm_row(x, r, w, dtype, rows ? rows[i] : i, C, eps, y + i * C, s)) ok[t] = 0;
+    }
+  };
+  const int64_t per = (n + threads - 1) / threads;
+  std::vector<std::thread> pool;
+  for (int t = 0; t < threads; ++t) {
+    const int64_t b = t * per, e = std::min(n, b + per);
+    if (b < e) pool.emplace_back(worker, t, b, e);
+  }
+  for (auto& th : pool) th.join();
+  for (int v : ok)
+    if (!v) return -1;
+  return 0;
+}
+
 }  // namespace
 
 extern "C" {
+
+// x, r (may be NULL: no residual), w: contiguous, dtype 0 = fp32, 1 = bf16 bit
+// patterns; x and r are [R, C], w is [C].  rows (may be NULL) selects the rows
+// computed.  y and s_out (may be NULL) are fp64 [n_rows or R, C].  0 on
+// success, -1 on an invalid argument (non-finite inputs, eps < 0, or a row
+// whose mean square plus eps is 0).
+int hfa_ref_rmsnorm(const void* x, const void* r, const void* w, int dtype, int64_t R, int64_t C, double eps,
+                    const int64_t* rows, int64_t n_rows, double* y, double* s_out, int threads) {
+  return rmsnorm_check_and_run(x, r, w, dtype, R, C, eps, rows, n_rows, y, s_out, threads);
+}
 
 // x: fp32 [R, C] contiguous; rows (may be NULL) selects the rows computed;
 // y: fp64 [n_rows or R, C].  0 on success, -1 on an invalid argument

@@ -422,3 +422,175 @@ SOFTMAX_CHECKS = [
     check_s10_softmax_rejects_bad_arguments,
 ]
 ALL_CHECKS.extend(SOFTMAX_CHECKS)
+
+
+# ---- RMS normalisation (TritonForge "Fused RMSNorm" card: RMSNorm(x) = x /
+# sqrt(sum_i x_i^2 / d + eps) * gamma; book chapter "Triton and kernel
+# fusion", section "Fused residual add + RMSNorm": s = x + residual, added
+# in fp32 by that section's kernel, is normalised and returned as well).
+
+def _golden_rmsnorm():
+    import os
+
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "rmsnorm_exact.txt")
+    fields = {}
+    for line in open(path):
+        line = line.strip()
+        if line and not line.startswith("#"):
+            key, *vals = line.split()
+            fields[key] = [float(v) for v in vals]
+    return fields
+
+
+def _row(vals):
+    return np.asarray(vals, np.float32).reshape(1, -1)
+
+
+# R1 -- the hand-derived rows of tests/golden/rmsnorm_exact.txt.
+def check_r1_rmsnorm_golden(orc):
+    g = _golden_rmsnorm()
+    y, s = orc.rmsnorm(_row(g["a_x"]), np.asarray(g["a_w"], np.float32), g["a_eps"][0])
+    np.testing.assert_allclose(y[0], np.asarray(g["a_y_over_sqrt2"]) * math.sqrt(2.0), rtol=1e-15, atol=0)
+    np.testing.assert_array_equal(s[0], g["a_x"])
+    y, _ = orc.rmsnorm(_row(g["b_x"]), np.asarray(g["b_w"], np.float32), g["b_eps"][0])
+    np.testing.assert_allclose(y[0], g["b_y"], rtol=1e-15, atol=0)
+    y, s = orc.rmsnorm(_row(g["c_x"]), np.asarray(g["c_w"], np.float32), g["c_eps"][0], residual=_row(g["c_r"]))
+    np.testing.assert_array_equal(s[0], g["c_s"])
+    rms = math.sqrt(g["c_rms_sq_num"][0] / g["c_rms_sq_den"][0])
+    np.testing.assert_allclose(y[0], np.asarray(g["c_s"]) / rms, rtol=1e-15, atol=0)
+
+
+# R2 -- with unit weight the output's mean square is ms / (ms + eps), ms the
+# input's mean square (computed here by numpy): pins the 1/d, eps inside the root.
+def check_r2_rmsnorm_output_mean_square(orc):
+    for C, eps in ((1, 0.25), (7, 0.5), (512, 0.5), (4097, 2.0)):
+        x = _rand((5, C), 40 + C, 1.0)
+        y, _ = orc.rmsnorm(x, np.ones(C, np.float32), eps)
+        ms = np.mean(x.astype(np.float64) ** 2, axis=1)
+        np.testing.assert_allclose(np.mean(y ** 2, axis=1), ms / (ms + eps), rtol=1e-13, atol=0)
+
+
+# R3 -- homogeneity: y(a x; a^2 eps) = y(x; eps), and with eps = 0 the output is
+# invariant to scaling the row (a a power of two, so a x is exact in fp32).
+def check_r3_rmsnorm_homogeneity(orc):
+    x = _rand((4, 300), 43, 1.0)
+    w = _rand((300,), 44, 1.0)
+    for a in (4.0, 0.125):
+        y1, _ = orc.rmsnorm(x, w, 0.3)
+        y2, _ = orc.rmsnorm((x * a).astype(np.float32), w, 0.3 * a * a)
+        np.testing.assert_allclose(y2, y1, rtol=1e-13, atol=1e-15)
+        y1, _ = orc.rmsnorm(x, w, 0.0)
+        y2, _ = orc.rmsnorm((x * a).astype(np.float32), w, 0.0)
+        np.testing.assert_allclose(y2, y1, rtol=1e-13, atol=1e-15)
+
+
+# R4 -- independent library routine: torch's fp64 rms_norm (the pages' parity
+# baseline being PyTorch eager), over several widths.
+def check_r4_rmsnorm_library_crosscheck(orc):
+    import torch.nn.functional as F
+
+    for C in (1, 7, 512, 2048, 4097):
+        x = _rand((6, C), 50 + C, 3.0)
+        w = (1.0 + 0.1 * _rand((C,), 60 + C)).astype(np.float32)
+        y, _ = orc.rmsnorm(x, w, 1e-6)
+        ref = F.rms_norm(torch.from_numpy(x.astype(np.float64)), (C,), torch.from_numpy(w.astype(np.float64)),
+                         eps=1e-6).numpy()
+        np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-14)
+
+
+# R5 -- the weight multiplies column by column: y(w) = y(1) * w, and permuting
+# the columns of x and w permutes the output's columns.
+def check_r5_rmsnorm_weight_columns(orc):
+    C = 257
+    x = _rand((3, C), 61, 2.0)
+    w = _rand((C,), 62, 1.0)
+    y1, _ = orc.rmsnorm(x, np.ones(C, np.float32), 1e-3)
+    yw, _ = orc.rmsnorm(x, w, 1e-3)
+    np.testing.assert_allclose(yw, y1 * w.astype(np.float64), rtol=1e-14, atol=1e-15)
+    perm = np.random.default_rng(63).permutation(C)
+    yp, _ = orc.rmsnorm(np.ascontiguousarray(x[:, perm]), np.ascontiguousarray(w[perm]), 1e-3)
+    np.testing.assert_allclose(yp, yw[:, perm], rtol=1e-14, atol=1e-15)
+
+
+# R6 -- the residual is added in fp32 (numpy float32 addition, IEEE round to
+# nearest even), and the output is the normalisation of that sum.
+def check_r6_rmsnorm_residual_fp32_sum(orc):
+    x = _rand((4, 1000), 64, 1.0)
+    r = _rand((4, 1000), 65, 1e-3)
+    w = _rand((1000,), 66, 1.0)
+    s32 = x + r  # float32 + float32 in numpy is one fp32 add
+    assert s32.dtype == np.float32
+    y, s = orc.rmsnorm(x, w, 1e-6, residual=r)
+    np.testing.assert_array_equal(s, s32.astype(np.float64))
+    assert np.any(s32.astype(np.float64) != x.astype(np.float64) + r.astype(np.float64))
+    y_ref, s_ref = orc.rmsnorm(s32, w, 1e-6)
+    np.testing.assert_array_equal(y, y_ref)
+    np.testing.assert_array_equal(s_ref, s)
+
+
+# R7 -- bf16 inputs are widened exactly: the result equals that of the widened
+# fp32 values (residual included).
+def check_r7_rmsnorm_bf16_widening(orc):
+    rng = np.random.default_rng(67)
+    xb = rng.integers(0x3c00, 0x4100, size=(3, 129)).astype(np.uint16)
+    xb[:, ::2] |= 0x8000
+    rb = rng.integers(0x3a00, 0x4000, size=(3, 129)).astype(np.uint16)
+    wb = rng.integers(0x3f00, 0x3fa0, size=(129,)).astype(np.uint16)
+    y, s = orc.rmsnorm(xb, wb, 1e-5, residual=rb)
+    y32, s32 = orc.rmsnorm(_widen_bf16(xb), _widen_bf16(wb), 1e-5, residual=_widen_bf16(rb))
+    np.testing.assert_array_equal(y, y32)
+    np.testing.assert_array_equal(s, s32)
+
+
+# R8 -- a row subset equals the same rows of the full result.
+def check_r8_rmsnorm_sampled_rows(orc):
+    x = _rand((9, 100), 68, 1.0)
+    r = _rand((9, 100), 69, 1.0)
+    w = _rand((100,), 70, 1.0)
+    y, s = orc.rmsnorm(x, w, 1e-6, residual=r)
+    rows = [8, 0, 5]
+    ys, ss = orc.rmsnorm(x, w, 1e-6, residual=r, rows=rows)
+    np.testing.assert_array_equal(ys, y[rows])
+    np.testing.assert_array_equal(ss, s[rows])
+
+
+# R9 -- one column: y = s / sqrt(s^2 + eps) * w, and sign(s) * w when eps = 0.
+def check_r9_rmsnorm_single_column(orc):
+    x = np.asarray([[3.0], [-0.5], [1e-3]], np.float32)
+    w = np.asarray([2.0], np.float32)
+    y, _ = orc.rmsnorm(x, w, 0.0)
+    np.testing.assert_allclose(y[:, 0], [2.0, -2.0, 2.0], rtol=1e-15, atol=0)
+    y, _ = orc.rmsnorm(x, w, 1.0)
+    xd = x[:, 0].astype(np.float64)
+    np.testing.assert_allclose(y[:, 0], 2.0 * xd / np.sqrt(xd * xd + 1.0), rtol=1e-15, atol=0)
+
+
+# R10 -- invalid arguments are rejected.
+def check_r10_rmsnorm_rejects_bad_arguments(orc):
+    x = _rand((2, 10), 71)
+    w = np.ones(10, np.float32)
+    bad = x.copy()
+    bad[1, 3] = np.inf
+    with pytest.raises(ValueError):
+        orc.rmsnorm(bad, w, 1e-6)
+    with pytest.raises(ValueError):
+        orc.rmsnorm(x, w, -1e-6)
+    with pytest.raises(ValueError):
+        orc.rmsnorm(np.zeros((2, 10), np.float32), w, 0.0)
+    with pytest.raises(ValueError):
+        orc.rmsnorm(x, w, 1e-6, rows=[0, 2])
+
+
+RMSNORM_CHECKS = [
+    check_r1_rmsnorm_golden,
+    check_r2_rmsnorm_output_mean_square,
+    check_r3_rmsnorm_homogeneity,
+    check_r4_rmsnorm_library_crosscheck,
+    check_r5_rmsnorm_weight_columns,
+    check_r6_rmsnorm_residual_fp32_sum,
+    check_r7_rmsnorm_bf16_widening,
+    check_r8_rmsnorm_sampled_rows,
+    check_r9_rmsnorm_single_column,
+    check_r10_rmsnorm_rejects_bad_arguments,
+]
+ALL_CHECKS.extend(RMSNORM_CHECKS)

@@ -34,6 +34,18 @@ MUTATIONS = {
     "softmax_online_rescale_sign": ("l * std::exp(m - m_new)", "l * std::exp(m_new - m)"),
     "softmax_sampled_row_index": ("const float* row = x + (rows ? rows[i] : i) * C;\n      if (chunk == 0)",
                                   "const float* row = x + i * C;\n      if (chunk == 0)"),
+    "rms_no_mean": ("std::sqrt(sq / static_cast<double>(C) + eps)", "std::sqrt(sq + eps)"),
+    "rms_eps_outside_root": ("std::sqrt(sq / static_cast<double>(C) + eps)",
+                             "(std::sqrt(sq / static_cast<double>(C)) + eps)"),
+    "rms_no_root": ("std::sqrt(sq / static_cast<double>(C) + eps)", "(sq / static_cast<double>(C) + eps)"),
+    "rms_abs_not_square": ("sq += s[j] * s[j];", "sq += std::fabs(s[j]);"),
+    "rms_dropped_first_square": ("sq += s[j] * s[j];", "if (j > 0) sq += s[j] * s[j];"),
+    "rms_weight_reversed": ("s[j] / denom * widen(w, dtype, j)", "s[j] / denom * widen(w, dtype, C - 1 - j)"),
+    "rms_residual_dropped": ("const float sum = a + b;", "const float sum = a;"),
+    "rms_residual_sign": ("const float sum = a + b;", "const float sum = a - b;"),
+    "rms_residual_in_fp64": ("const float sum = a + b;\n  return static_cast<double>(sum);",
+                             "return static_cast<double>(a) + static_cast<double>(b);"),
+    "rms_sampled_row_index": ("rmsnorm_row(x, r, w, dtype, rows ? rows[i] : i,", "rmsnorm_row(x, r, w, dtype, i,"),
 }
 
 

@@ -88,3 +88,8 @@ def test_golden_exact_rational(orc):
 @pytest.mark.parametrize("check", C.SOFTMAX_CHECKS, ids=lambda f: f.__name__[6:])
 def test_softmax_pins(orc, check):
     check(orc)
+
+
+@pytest.mark.parametrize("check", C.RMSNORM_CHECKS, ids=lambda f: f.__name__[6:])
+def test_rmsnorm_pins(orc, check):
+    check(orc)
