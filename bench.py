@@ -48,6 +48,7 @@ def log(msg: str) -> None:
 OP_SOURCES = {
     "attn": ("common.hpp", "api_util.hpp", "attn_bf16.hpp", "attn_f32.hpp", "hfa_api.hip"),
     "softmax": ("common.hpp", "api_util.hpp", "softmax_rows.hpp", "softmax_api.hip"),
+    "rmsnorm": ("common.hpp", "api_util.hpp", "rmsnorm.hpp", "rmsnorm_api.hip"),
 }
 
 
@@ -163,43 +164,105 @@ def softmax_key(sw) -> str:
     return f"softmax_rows_f32_{sw.rows}x{sw.cols}"
 
 
-def load_softmax_traffic(sw):
-    try:
-        with open(TRAFFIC_FILE) as f:
-            entry = json.load(f).get(softmax_key(sw))
-    except (OSError, ValueError):
-        return None
-    if not entry or entry.get("src_digest") != kernel_source_digest("softmax"):
-        return None
-    return entry
+def rmsnorm_key(rw) -> str:
+    return f"rmsnorm_{rw.dtype}_{rw.rows}x{rw.cols}" + ("_res" if rw.residual else "")
 
 
-def time_softmax(sw, steps: int, warmup: int):
-    """hfa_softmax_rows on one resident fp32 matrix: ms per launch and algorithmic GB/s."""
+def _softmax_launcher(sw):
     import torch
 
     import fa2_fwd_amd as hfa
 
     x = sw.inputs().cuda()
     y = torch.empty_like(x)
+    return lambda stream: hfa.softmax_rows(x, out=y, stream=stream)
+
+
+def _rmsnorm_launcher(rw):
+    import torch
+
+    import fa2_fwd_amd as hfa
+
+    x, r, w = (None if t is None else t.cuda() for t in rw.inputs())
+    y = torch.empty_like(x)
+    s = torch.empty_like(x) if r is not None else None
+    return lambda stream: hfa.rmsnorm(x, w, rw.eps, residual=r, out=y, residual_out=s, stream=stream)
+
+
+def _softmax_oracle_rows(sw):
+    import oracle
+
+    x = sw.inputs().numpy()
+    return lambda rows, threads: oracle.softmax_rows(x, rows=rows, threads=threads), "fp64 definition"
+
+
+def _rmsnorm_oracle_rows(rw):
+    import numpy as np
+    import torch
+
+    import oracle
+
+    def host(t):
+        if t is None:
+            return None
+        t = t.contiguous()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    x, r, w = (host(t) for t in rw.inputs())
+    return (lambda rows, threads: oracle.rmsnorm(x, w, rw.eps, residual=r, rows=rows, threads=threads),
+            "fp32 residual sum, fp64 normalisation")
+
+
+# The HBM-bound operations timed beside the attention forward: their workloads,
+# the marker of their kernels' names in a trace, and how to launch and check them.
+HBM_OPS = {
+    "softmax": dict(configs="SOFTMAX_CONFIGS", marker="softmax_rows", key=softmax_key,
+                    launcher=_softmax_launcher, oracle_rows=_softmax_oracle_rows, json_key="softmax_rows"),
+    "rmsnorm": dict(configs="RMSNORM_CONFIGS", marker="rmsnorm_kernel", key=rmsnorm_key,
+                    launcher=_rmsnorm_launcher, oracle_rows=_rmsnorm_oracle_rows, json_key="rmsnorm"),
+}
+
+
+def hbm_configs(op: str):
+    from fa2_fwd_amd import workloads as W
+
+    return getattr(W, HBM_OPS[op]["configs"])
+
+
+def load_op_traffic(op: str, wl):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            entry = json.load(f).get(HBM_OPS[op]["key"](wl))
+    except (OSError, ValueError):
+        return None
+    if not entry or entry.get("src_digest") != kernel_source_digest(op):
+        return None
+    return entry
+
+
+def time_hbm_op(op: str, wl, steps: int, warmup: int):
+    """One HBM-bound operation on inputs resident in HBM: ms per launch and algorithmic GB/s."""
+    import torch
+
+    launch = HBM_OPS[op]["launcher"](wl)
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
-        hfa.softmax_rows(x, out=y, stream=stream)
+        launch(stream)
     torch.cuda.synchronize()
     events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     for i in range(steps):
         events[i].record(stream)
-        hfa.softmax_rows(x, out=y, stream=stream)
+        launch(stream)
     events[steps].record(stream)
     torch.cuda.synchronize()
     ms = events[0].elapsed_time(events[steps]) / steps
     per = sorted(events[i].elapsed_time(events[i + 1]) for i in range(steps))
-    gbs = sw.algorithmic_bytes / (ms * 1e-3) / 1e9
-    log(f"[bench] {sw.describe()}: {ms:.4f} ms/launch, {gbs:.0f} GB/s of algorithmic bytes, "
+    gbs = wl.algorithmic_bytes / (ms * 1e-3) / 1e9
+    log(f"[bench] {wl.describe()}: {ms:.4f} ms/launch, {gbs:.0f} GB/s of algorithmic bytes, "
         f"{100 * gbs / HBM_PEAK_GBS:.1f}% of HBM peak")
-    traffic = load_softmax_traffic(sw)
+    traffic = load_op_traffic(op, wl)
     return {
-        "workload": sw.describe(),
+        "workload": wl.describe(),
         "ms_per_step": round(ms, 5),
         "ms_median": round(per[len(per) // 2], 5),
         "ms_min": round(per[0], 5),
@@ -210,34 +273,34 @@ def time_softmax(sw, steps: int, warmup: int):
             "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": None if traffic is None else int(traffic["hbm_bytes_per_launch"]),
-            "algorithmic_bytes": sw.algorithmic_bytes,
-            "kernel": softmax_key(sw),
+            "algorithmic_bytes": wl.algorithmic_bytes,
+            "kernel": HBM_OPS[op]["key"](wl),
         },
     }
 
 
-def softmax_cpu_baseline(sw, target_s: float):
-    """The fp64 oracle on an evenly spaced sample of rows, in algorithmic GB/s."""
+def hbm_op_cpu_baseline(op: str, wl, target_s: float):
+    """The oracle on an evenly spaced sample of rows, in algorithmic GB/s."""
     import numpy as np
 
     import oracle
 
-    x = sw.inputs().numpy()
+    run_rows, what = HBM_OPS[op]["oracle_rows"](wl)
     threads = oracle.default_threads()
 
     def run(n):
-        rows = np.linspace(0, sw.rows - 1, n).round().astype(np.int64)
+        rows = np.linspace(0, wl.rows - 1, n).round().astype(np.int64)
         t0 = time.perf_counter()
-        oracle.softmax_rows(x, rows=rows, threads=threads)
+        run_rows(rows, threads)
         return time.perf_counter() - t0
 
-    t1 = run(min(sw.rows, 16))
-    n = int(min(sw.rows, max(16, round(16 * target_s / max(t1, 1e-6)))))
+    t1 = run(min(wl.rows, 16))
+    n = int(min(wl.rows, max(16, round(16 * target_s / max(t1, 1e-6)))))
     t = run(n)
-    gbs = 2 * n * sw.cols * 4 / t / 1e9
-    log(f"[bench] oracle softmax: {n} rows in {t:.2f} s on {threads} threads -> {gbs:.2f} GB/s")
+    gbs = wl.algorithmic_bytes * n / wl.rows / t / 1e9
+    log(f"[bench] oracle {op}: {n} rows in {t:.2f} s on {threads} threads -> {gbs:.2f} GB/s")
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} of {sw.rows} rows (evenly spaced), fp64 definition; {t:.2f} s"}
+            "sample": f"{n} of {wl.rows} rows (evenly spaced), {what}; {t:.2f} s"}
 
 
 def _sclk_files():
@@ -338,21 +401,20 @@ def cpu_baseline(w, target_s: float):
     }
 
 
-def profile_pass_softmax(sw, launches: int) -> None:
-    """A few softmax launches and one device copy of COPY_BYTES, for counter runs."""
+def profile_pass_hbm_op(op: str, wl, launches: int) -> None:
+    """A few launches of an HBM-bound operation and one device copy of COPY_BYTES, for counter runs."""
     import torch
 
-    import fa2_fwd_amd as hfa
-
-    x = sw.inputs().cuda()
+    launch = HBM_OPS[op]["launcher"](wl)
+    stream = torch.cuda.current_stream()
     for _ in range(launches):
-        hfa.softmax_rows(x)
-    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=x.device)
+        launch(stream)
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
-    log(f"[profile] {launches} launches of {sw.describe()} and one {COPY_BYTES} B copy done")
+    log(f"[profile] {launches} launches of {wl.describe()} and one {COPY_BYTES} B copy done")
 
 
 def profile_pass(w, launches: int) -> None:
@@ -390,9 +452,9 @@ def _read_counter(dirpath: str, counter: str):
 
 def summarize_pmc(w, fetch_dir: str, write_dir: str, op: str = "attn") -> None:
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the measured kernel (attention, or the
-    row softmax when op == "softmax"), each scaled by what the same counter reads for the
-    copy of known size."""
-    marker = "attn_fwd" if op == "attn" else "softmax_rows"
+    HBM-bound operation `op`), each scaled by what the same counter reads for the copy of
+    known size."""
+    marker = "attn_fwd" if op == "attn" else HBM_OPS[op]["marker"]
     result = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _read_counter(d, counter)
@@ -414,7 +476,7 @@ def summarize_pmc(w, fetch_dir: str, write_dir: str, op: str = "attn") -> None:
         with open(TRAFFIC_FILE) as f:
             table = json.load(f)
     total = result["FETCH_SIZE"]["bytes_per_launch"] + result["WRITE_SIZE"]["bytes_per_launch"]
-    key = kernel_key(w) + f"_N{w.N}" if op == "attn" else softmax_key(w)
+    key = kernel_key(w) + f"_N{w.N}" if op == "attn" else HBM_OPS[op]["key"](w)
     alg = algorithmic_bytes(w) if op == "attn" else w.algorithmic_bytes
     table[key] = {
         "workload": w.describe(),
@@ -445,20 +507,25 @@ def main() -> int:
     ap.add_argument("--profile-pass", action="store_true")
     ap.add_argument("--launches", type=int, default=3)
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
-    ap.add_argument("--op", choices=("attn", "softmax"), default="attn",
-                    help="kernel for --profile-pass / --summarize-pmc / --softmax-only (softmax: --config 1 or 2)")
-    ap.add_argument("--softmax-only", action="store_true", help="time only the row softmax workload --config")
+    ap.add_argument("--op", choices=("attn", "softmax", "rmsnorm"), default="attn",
+                    help="kernel for --profile-pass / --summarize-pmc / --op-only (--config numbers that "
+                         "op's workloads)")
+    ap.add_argument("--op-only", action="store_true", help="time only workload --config of --op")
+    ap.add_argument("--softmax-only", action="store_true", help="same as --op softmax --op-only")
     ap.add_argument("--no-softmax", action="store_true", help="skip the row softmax workloads")
+    ap.add_argument("--no-rmsnorm", action="store_true", help="skip the RMS normalisation workloads")
     args = ap.parse_args()
 
     from fa2_fwd_amd import workloads as W
 
-    if args.op == "softmax" and (args.summarize_pmc or args.profile_pass):
-        sw = W.SOFTMAX_CONFIGS[args.config]
+    if args.softmax_only:
+        args.op, args.op_only = "softmax", True
+    if args.op != "attn" and (args.summarize_pmc or args.profile_pass):
+        wl = hbm_configs(args.op)[args.config]
         if args.summarize_pmc:
-            summarize_pmc(sw, *args.summarize_pmc, op="softmax")
+            summarize_pmc(wl, *args.summarize_pmc, op=args.op)
         else:
-            profile_pass_softmax(sw, args.launches)
+            profile_pass_hbm_op(args.op, wl, args.launches)
         return 0
     w = W.CONFIGS[args.config]
     if args.summarize_pmc:
@@ -477,8 +544,12 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
-    if args.softmax_only:
-        print(json.dumps(time_softmax(W.SOFTMAX_CONFIGS[args.config], args.steps, args.warmup)), flush=True)
+    if args.op_only:
+        if args.op == "attn":
+            print("--op-only needs --op softmax or --op rmsnorm", file=sys.stderr)
+            return 2
+        print(json.dumps(time_hbm_op(args.op, hbm_configs(args.op)[args.config], args.steps, args.warmup)),
+              flush=True)
         return 0
     main_res = time_gpu(w, args.steps, args.warmup)
     secondary = None
@@ -518,15 +589,18 @@ def main() -> int:
     sclk = None if args.no_sclk else observed_sclk(w, 0.5)
     if sclk is not None:
         log(f"[bench] shader clock during {w.describe()}: {sclk:.0f} MHz (median of sysfs samples)")
-    softmax = None
-    if not args.no_softmax:
-        softmax = []
-        for n, sw in sorted(W.SOFTMAX_CONFIGS.items()):
-            entry = time_softmax(sw, args.steps, args.warmup)
+    hbm = {}
+    for op, skip, baseline_cfg in (("softmax", args.no_softmax, 1), ("rmsnorm", args.no_rmsnorm, 3)):
+        if skip:
+            continue
+        entries = []
+        for n, wl in sorted(hbm_configs(op).items()):
+            entry = time_hbm_op(op, wl, args.steps, args.warmup)
             entry["config"] = n
-            if n == 1 and not args.no_cpu_baseline:
-                entry["cpu_baseline"] = softmax_cpu_baseline(sw, 3.0)
-            softmax.append(entry)
+            if n == baseline_cfg and not args.no_cpu_baseline:
+                entry["cpu_baseline"] = hbm_op_cpu_baseline(op, wl, 3.0)
+            entries.append(entry)
+        hbm[HBM_OPS[op]["json_key"]] = entries
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
     props = torch.cuda.get_device_properties(0)
     line = {
@@ -549,7 +623,8 @@ def main() -> int:
         "cpu_baseline": cpu,
         "secondary": secondary,
         "all_configs": all_configs,
-        "softmax_rows": softmax,
+        "softmax_rows": hbm.get("softmax_rows"),
+        "rmsnorm": hbm.get("rmsnorm"),
         "observed_sclk_mhz": sclk,
         "device": getattr(props, "gcnArchName", props.name),
     }

@@ -29,9 +29,10 @@ HFA_ERR_ALIGN = 5
 HFA_ERR_ALIAS = 6
 HFA_ERR_NO_DEVICE = 7
 HFA_ERR_LAUNCH = 8
+HFA_ERR_EPS = 9
 
 EXPORTED = ("hfa_attn_fwd", "hfa_status_str", "hfa_block_rows", "hfa_attn_fwd_graph_create", "hfa_graph_launch",
-            "hfa_graph_destroy", "hfa_softmax_rows")
+            "hfa_graph_destroy", "hfa_softmax_rows", "hfa_rmsnorm")
 
 _lib = None
 
@@ -73,6 +74,8 @@ def load_library(path: str | Path | None = None) -> ctypes.CDLL:
     lib.hfa_graph_destroy.restype = None
     lib.hfa_softmax_rows.argtypes = [vp, vp, i64, i64, vp]
     lib.hfa_softmax_rows.restype = ctypes.c_int
+    lib.hfa_rmsnorm.argtypes = [vp, vp, vp, vp, vp, i64, i64, ctypes.c_float, ctypes.c_int, vp]
+    lib.hfa_rmsnorm.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -131,6 +134,54 @@ def softmax_rows(x, out=None, stream=None):
     return out
 
 
+def hfa_rmsnorm(x, residual, weight, y, residual_out, rows, cols, eps, dtype, stream) -> int:
+    """Raw C-ABI call: pointers as ints (device addresses) or None; returns the status."""
+    return load_library().hfa_rmsnorm(x, residual, weight, y, residual_out, rows, cols, eps, dtype, stream)
+
+
+def rmsnorm(x, weight, eps: float = 1e-6, residual=None, out=None, residual_out=None, stream=None):
+    """RMS normalisation over the last dim of a contiguous float32 or bfloat16 device tensor.
+
+    ``y = s / sqrt(mean(s**2) + eps) * weight`` with ``s = x + residual`` (``s = x`` without a
+    residual).  Returns ``y``, or ``(y, s)`` when ``residual`` is given.  ``out`` and
+    ``residual_out`` may be given to write into caller buffers, and may be ``x`` or ``residual``
+    themselves (in place).  Rows are limited to 65536 elements.
+    """
+    import torch
+
+    tensors = [x, weight] + ([residual] if residual is not None else [])
+    if any(not isinstance(t, torch.Tensor) for t in tensors):
+        raise ValueError("rmsnorm takes torch tensors")
+    if x.ndim < 1 or weight.ndim != 1 or weight.shape[0] != x.shape[-1]:
+        raise ValueError("rmsnorm needs x [..., C] and weight [C]")
+    code = _dtype_code(x)
+    if any(t.dtype != x.dtype for t in tensors):
+        raise ValueError("x, weight and residual must share one dtype")
+    if residual is not None and residual.shape != x.shape:
+        raise ValueError("residual must have x's shape")
+    if any(not t.is_cuda or t.device != x.device for t in tensors) or any(not t.is_contiguous() for t in tensors):
+        raise ValueError("rmsnorm needs contiguous tensors on one GPU")
+
+    def _buf(t):
+        if t is None:
+            return torch.empty_like(x)
+        if t.shape != x.shape or t.dtype != x.dtype or t.device != x.device or not t.is_contiguous():
+            raise ValueError("output buffers must be contiguous tensors like x")
+        return t
+
+    out = _buf(out)
+    res_out = _buf(residual_out) if residual is not None else None
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    with torch.cuda.device(x.device):
+        st = hfa_rmsnorm(x.data_ptr(), None if residual is None else residual.data_ptr(), weight.data_ptr(),
+                         out.data_ptr(), None if res_out is None else res_out.data_ptr(), rows, cols, float(eps),
+                         code, _stream_handle(stream, x.device))
+    if st != HFA_OK:
+        raise HfaError(st)
+    return out if residual is None else (out, res_out)
+
+
 def _dtype_code(t) -> int:
     import torch
 
@@ -138,7 +189,7 @@ def _dtype_code(t) -> int:
         return HFA_F32
     if t.dtype == torch.bfloat16:
         return HFA_BF16
-    raise ValueError(f"attn_fwd supports float32 and bfloat16, got {t.dtype}")
+    raise ValueError(f"float32 and bfloat16 are supported, got {t.dtype}")
 
 
 def _prepare(q, k, v, scale, out, lse):

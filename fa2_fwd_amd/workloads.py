@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the attention forward and the row softmax.
+"""Seeded synthetic inputs for the attention forward, the row softmax and the RMS normalisation.
 
 This module only draws random numbers and lays them out; it holds none of the
 attention arithmetic, so both the GPU path's tests and the CPU oracle can take
@@ -87,6 +87,57 @@ class SoftmaxWorkload:
 SOFTMAX_CONFIGS = {
     1: SoftmaxWorkload("softmax1", 4096, 32000, 101),
     2: SoftmaxWorkload("softmax2", 256, 262144, 102),
+}
+
+
+@dataclass(frozen=True)
+class RmsNormWorkload:
+    """Residual add + RMS normalisation of seeded [rows, cols] rows.
+
+    Draw order: x, residual (both N(0, 1)), then weight = 1 + 0.1 N(0, 1), all fp32,
+    rounded to bf16 (nearest even) for bf16 workloads."""
+
+    name: str
+    rows: int
+    cols: int
+    dtype: str  # "f32" or "bf16"
+    seed: int
+    residual: bool = True
+    eps: float = 1e-6
+
+    @property
+    def elt(self) -> int:
+        return 4 if self.dtype == "f32" else 2
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """x (and the residual) read once, y (and the sum) written once, the weight read once."""
+        arrays = 4 if self.residual else 2
+        return (arrays * self.rows * self.cols + self.cols) * self.elt
+
+    def describe(self) -> str:
+        res = " +residual" if self.residual else ""
+        return f"rmsnorm {self.rows}x{self.cols} {self.dtype}{res} seed={self.seed}"
+
+    def inputs(self):
+        """Host tensors (x, residual or None, weight) in the workload's dtype."""
+        g = torch.Generator("cpu").manual_seed(int(self.seed))
+        x = torch.randn(self.rows, self.cols, generator=g, dtype=torch.float32)
+        r = torch.randn(self.rows, self.cols, generator=g, dtype=torch.float32) if self.residual else None
+        w = 1.0 + 0.1 * torch.randn(self.cols, generator=g, dtype=torch.float32)
+        dt = torch_dtype(self.dtype)
+        return x.to(dt), (r.to(dt) if r is not None else None), w.to(dt)
+
+
+# RMS normalisation workloads: the widths of the TritonForge benchmark table
+# (N = 512, 2048, 8192, fp32; its row counts are not given), each sized to
+# 2^26 elements, and a bf16 [16384, 8192] transformer residual stream.  All
+# take the fused residual form of the book chapter "Triton and kernel fusion".
+RMSNORM_CONFIGS = {
+    1: RmsNormWorkload("rmsnorm1", 131072, 512, "f32", 201),
+    2: RmsNormWorkload("rmsnorm2", 32768, 2048, "f32", 202),
+    3: RmsNormWorkload("rmsnorm3", 8192, 8192, "f32", 203),
+    4: RmsNormWorkload("rmsnorm4", 16384, 8192, "bf16", 204),
 }
 
 

@@ -57,7 +57,8 @@ typedef enum {
   HFA_ERR_ALIGN = 5,       /* q, k, v, o not 16-byte aligned, or lse not 4-byte aligned */
   HFA_ERR_ALIAS = 6,       /* o or lse overlaps q, k, v or each other */
   HFA_ERR_NO_DEVICE = 7,   /* no HIP device is current, or it is not gfx950 */
-  HFA_ERR_LAUNCH = 8       /* the kernel launch itself failed */
+  HFA_ERR_LAUNCH = 8,      /* the kernel launch itself failed */
+  HFA_ERR_EPS = 9          /* hfa_rmsnorm: eps is not a finite value > 0 */
 } hfa_status;
 
 /* Attention forward.
@@ -144,6 +145,44 @@ void hfa_graph_destroy(hfa_graph g);
  * HFA_ERR_LAUNCH if the launch fails.  Asynchronous on `stream`; allocates
  * nothing. */
 hfa_status hfa_softmax_rows(const float* x, float* y, int64_t rows, int64_t cols, void* stream);
+
+/* Fused residual add + RMS normalisation of each row:
+ *
+ *     s[r, :] = x[r, :] + residual[r, :]     (s = x when residual is NULL)
+ *     y[r, :] = s[r, :] / sqrt(sum_j s[r, j]^2 / cols + eps) * weight[:]
+ *
+ * The normalisation is the TritonForge page's "Fused RMSNorm" card formula
+ * (x / sqrt(sum_i x_i^2 / d + eps) scaled elementwise by gamma); the residual
+ * form and the second output s are the book chapter "Triton and kernel
+ * fusion", section "Fused residual add + RMSNorm" (x and residual read once,
+ * y and s written once).  Each row is held in registers by one group of
+ * threads, so rows are limited to 65536 columns, the width up to which that
+ * chapter's engine takes the fused kernel.
+ *
+ * Precision: elements are fp32 or bf16 (dtype applies to every array); the
+ * sum is one fp32 add of the upcast operands, the mean square, root and
+ * products are fp32, and bf16 outputs are rounded once to nearest even.  y is
+ * normalised from the fp32 sum, not from its stored (rounded) copy.
+ *
+ *   x, residual   device, [rows, cols] contiguous; residual may be NULL.
+ *   weight        device, [cols] contiguous (gamma).
+ *   y             device, [rows, cols]: the normalised rows.
+ *   residual_out  device, [rows, cols]: receives s; required when residual is
+ *                 given, ignored otherwise.
+ *   rows, cols    rows >= 1, rows < 2^31; 1 <= cols <= 65536.
+ *   eps           finite and > 0 (1e-6 is the pages' default).
+ *   dtype         HFA_F32 or HFA_BF16.
+ *   stream        a hipStream_t, passed as a pointer; NULL selects the null stream.
+ *
+ * Every pointer must be aligned to the element size (16-byte alignment with
+ * cols a multiple of 16 bytes takes 16-byte accesses).  y and residual_out may
+ * each be exactly x or residual (in place) but must not partly overlap them,
+ * and must overlap neither weight nor each other.  Validation precedes any HIP
+ * call: HFA_ERR_NULL, HFA_ERR_UNSUPPORTED, HFA_ERR_SHAPE, HFA_ERR_EPS,
+ * HFA_ERR_ALIGN, HFA_ERR_ALIAS, HFA_ERR_NO_DEVICE, then HFA_ERR_LAUNCH if the
+ * launch fails.  Asynchronous on `stream`; allocates nothing. */
+hfa_status hfa_rmsnorm(const void* x, const void* residual, const void* weight, void* y, void* residual_out,
+                       int64_t rows, int64_t cols, float eps, hfa_dtype dtype, void* stream);
 
 #ifdef __cplusplus
 }

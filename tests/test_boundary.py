@@ -58,7 +58,7 @@ def test_library_is_gfx950_only(tmp_path):
 
 
 def test_status_strings_distinct():
-    codes = range(0, 9)
+    codes = range(0, 10)
     strs = [hfa.hfa_status_str(c) for c in codes]
     assert len(set(strs)) == len(strs)
     assert hfa.hfa_status_str(99) == "unknown status"
@@ -190,3 +190,66 @@ def test_softmax_rows_rejects_before_any_hip_call(kw, status):
     a = dict(x=0x100000, y=0x900000, rows=4, cols=1000, stream=None)
     a.update(kw)
     assert hfa.hfa_softmax_rows(a["x"], a["y"], a["rows"], a["cols"], a["stream"]) == status
+
+
+RMS_GOOD = dict(x=0x100000, r=0x200000, w=0x300000, y=0x400000, s=0x500000, rows=4, cols=1000, eps=1e-6,
+                dtype=hfa.HFA_F32, stream=None)
+
+
+def _rms(**kw):
+    a = dict(RMS_GOOD)
+    a.update(kw)
+    return hfa.hfa_rmsnorm(a["x"], a["r"], a["w"], a["y"], a["s"], a["rows"], a["cols"], a["eps"], a["dtype"],
+                           a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), hfa.HFA_ERR_NULL),
+    (dict(w=None), hfa.HFA_ERR_NULL),
+    (dict(y=None), hfa.HFA_ERR_NULL),
+    (dict(s=None), hfa.HFA_ERR_NULL),
+    (dict(dtype=5), hfa.HFA_ERR_UNSUPPORTED),
+    (dict(rows=0), hfa.HFA_ERR_SHAPE),
+    (dict(cols=0), hfa.HFA_ERR_SHAPE),
+    (dict(cols=65537), hfa.HFA_ERR_SHAPE),
+    (dict(rows=1 << 31), hfa.HFA_ERR_SHAPE),
+    (dict(eps=0.0), hfa.HFA_ERR_EPS),
+    (dict(eps=-1e-6), hfa.HFA_ERR_EPS),
+    (dict(eps=float("inf")), hfa.HFA_ERR_EPS),
+    (dict(eps=float("nan")), hfa.HFA_ERR_EPS),
+    (dict(x=0x100002), hfa.HFA_ERR_ALIGN),
+    (dict(w=0x300001, dtype=hfa.HFA_BF16), hfa.HFA_ERR_ALIGN),
+    (dict(s=0x500002), hfa.HFA_ERR_ALIGN),
+    (dict(y=0x100000 + 4), hfa.HFA_ERR_ALIAS),
+    (dict(y=0x200000 - 8), hfa.HFA_ERR_ALIAS),
+    (dict(y=0x300000 - 16), hfa.HFA_ERR_ALIAS),
+    (dict(s=0x300000 + 4), hfa.HFA_ERR_ALIAS),
+    (dict(s=0x400000), hfa.HFA_ERR_ALIAS),
+    (dict(s=0x400000 + 400), hfa.HFA_ERR_ALIAS),
+])
+def test_rmsnorm_rejects_before_any_hip_call(kw, status):
+    assert _rms(**kw) == status
+
+
+def test_rmsnorm_accepts_in_place_and_no_residual():
+    if torch.cuda.is_available():
+        pytest.skip("would launch on a visible GPU with fake pointers")
+    ok = hfa.HFA_ERR_NO_DEVICE  # validation passed; no device here
+    assert _rms(y=RMS_GOOD["x"]) == ok
+    assert _rms(s=RMS_GOOD["x"]) == ok
+    assert _rms(y=RMS_GOOD["r"], s=RMS_GOOD["x"]) == ok
+    assert _rms(r=None, s=None) == ok
+    assert _rms(r=None, s=0x300000) == ok  # residual_out is ignored without a residual
+    assert _rms(x=0x100002, w=0x300002, y=0x400002, r=None, dtype=hfa.HFA_BF16) == ok
+    assert _rms(cols=65536, rows=1) == ok
+
+
+def test_rmsnorm_binding_value_errors():
+    x = torch.zeros(4, 16)
+    w = torch.ones(16)
+    with pytest.raises(ValueError):
+        hfa.rmsnorm(x, w)  # host tensors
+    with pytest.raises(ValueError):
+        hfa.rmsnorm(x, torch.ones(15))
+    with pytest.raises(ValueError):
+        hfa.rmsnorm(x.double(), w.double())
