@@ -13,11 +13,13 @@
 // ITEMS slots of 16 bytes of the row in registers, so x and the residual are
 // read once: the sum of squares is reduced over the group (wave shuffles, then
 // LDS across the group's waves) and the same registers are normalised and
-// written.  Element i of a row is read and written by one thread, and all its
+// written (16-byte outputs with non-temporal stores: nothing reads them back
+// here).  Element i of a row is read and written by one thread, and all its
 // reads precede its writes, so y and s may be written over x or the residual.
 #pragma once
 
 #include "common.hpp"
+#include "hbm_io.hpp"
 
 namespace hfa {
 
@@ -30,12 +32,12 @@ struct RmsElt<float> {
   __device__ static float load(const float* p) { return *p; }
   __device__ static void store(float* p, float v) { *p = v; }
   __device__ static void load_slot(const float* p, float (&v)[4]) {
-    const f32x4 q = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 q = load16<false>(reinterpret_cast<const f32x4*>(p));
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = q[e];
   }
   __device__ static void store_slot(float* p, const float (&v)[4]) {
-    *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+    store16<true>(reinterpret_cast<f32x4*>(p), f32x4{v[0], v[1], v[2], v[3]});
   }
 };
 
@@ -45,7 +47,7 @@ struct RmsElt<__bf16> {
   __device__ static float load(const __bf16* p) { return static_cast<float>(*p); }
   __device__ static void store(__bf16* p, float v) { *p = static_cast<__bf16>(v); }
   __device__ static void load_slot(const __bf16* p, float (&v)[8]) {
-    const bf16x8 q = *reinterpret_cast<const bf16x8*>(p);
+    const bf16x8 q = load16<false>(reinterpret_cast<const bf16x8*>(p));
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = static_cast<float>(q[e]);
   }
@@ -53,7 +55,7 @@ struct RmsElt<__bf16> {
     bf16x8 q;
 #pragma unroll
     for (int e = 0; e < 8; ++e) q[e] = static_cast<__bf16>(v[e]);
-    *reinterpret_cast<bf16x8*>(p) = q;
+    store16<true>(reinterpret_cast<bf16x8*>(p), q);
   }
 };
 

@@ -13,18 +13,21 @@
 // first across the 64 lanes of a wave, then across the waves through LDS.
 //
 //  * Resident path (cols <= NT * 4 * ITEMS): the thread's elements stay in
-//    registers between the reduction and the output: x is read once.
+//    registers between the reduction and the output: x is read once, with
+//    non-temporal loads.
 //  * Streaming path: the thread's running pair is updated chunk by chunk
 //    while x streams through (UNROLL 16-byte loads in flight per thread), then
 //    x is read a second time to write y.
 //
-// Exponentials are exp2 of (x - M) * log2(e), the difference taken first so
-// that large |x| loses no accuracy.  Element i of a row is read and written by
+// y is written with non-temporal stores.  Exponentials are exp2 of
+// (x - M) * log2(e), the difference taken first so that large |x| loses no
+// accuracy.  Element i of a row is read and written by
 // the same thread, and every read precedes the reduction barrier, so y may be
 // x itself.
 #pragma once
 
 #include "common.hpp"
+#include "hbm_io.hpp"
 
 namespace hfa {
 
@@ -84,14 +87,16 @@ __device__ __forceinline__ int64_t slot_index(int64_t base, int s, int tid, int 
   return VEC ? base + (static_cast<int64_t>(s) * NT + tid) * 4 + e : base + (static_cast<int64_t>(s) * 4 + e) * NT + tid;
 }
 
-template <int NT, bool VEC, int SLOTS>
+// NT_LOAD: the row is read only once (resident path), so the read is
+// non-temporal; the streaming path reads x twice and keeps it cacheable.
+template <int NT, bool VEC, int SLOTS, bool NT_LOAD>
 __device__ __forceinline__ void load_slots(const float* xr, int64_t base, int64_t cols, int tid, float (&v)[SLOTS * 4]) {
 #pragma unroll
   for (int s = 0; s < SLOTS; ++s) {
     if (VEC) {
       const int64_t i0 = slot_index<NT, true>(base, s, tid, 0);
       if (i0 < cols) {
-        const f32x4 q = *reinterpret_cast<const f32x4*>(xr + i0);
+        const f32x4 q = load16<NT_LOAD>(reinterpret_cast<const f32x4*>(xr + i0));
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[4 * s + e] = q[e];
       } else {
@@ -118,7 +123,7 @@ __device__ __forceinline__ void store_slots(float* yr, int64_t base, int64_t col
     for (int e = 0; e < 4; ++e) o[e] = exp2_hw((v[4 * s + e] - M) * kLog2eF) * inv;
     if (VEC) {
       const int64_t i0 = slot_index<NT, true>(base, s, tid, 0);
-      if (i0 < cols) *reinterpret_cast<f32x4*>(yr + i0) = f32x4{o[0], o[1], o[2], o[3]};
+      if (i0 < cols) store16<true>(reinterpret_cast<f32x4*>(yr + i0), f32x4{o[0], o[1], o[2], o[3]});
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(NT) void softmax_rows_resident_kernel(const float* 
   const float* xr = x + row * cols;
   float* yr = y + row * cols;
   float v[ITEMS * 4];
-  load_slots<NT, VEC, ITEMS>(xr, 0, cols, tid, v);
+  load_slots<NT, VEC, ITEMS, true>(xr, 0, cols, tid, v);
   const SoftmaxPair p = merge_workgroup<NT>(fold_values(SoftmaxPair{-INFINITY, 0.0f}, v), lds);
   store_slots<NT, VEC, ITEMS>(yr, 0, cols, tid, v, p.m, 1.0f / p.l);
 }
@@ -155,14 +160,14 @@ __global__ __launch_bounds__(NT) void softmax_rows_stream_kernel(const float* x,
   SoftmaxPair p = {-INFINITY, 0.0f};
   for (int64_t base = 0; base < cols; base += STEP) {
     float v[UNROLL * 4];
-    load_slots<NT, VEC, UNROLL>(xr, base, cols, tid, v);
+    load_slots<NT, VEC, UNROLL, false>(xr, base, cols, tid, v);
     p = fold_values(p, v);
   }
   p = merge_workgroup<NT>(p, lds);
   const float inv = 1.0f / p.l;
   for (int64_t base = 0; base < cols; base += STEP) {
     float v[UNROLL * 4];
-    load_slots<NT, VEC, UNROLL>(xr, base, cols, tid, v);
+    load_slots<NT, VEC, UNROLL, false>(xr, base, cols, tid, v);
     store_slots<NT, VEC, UNROLL>(yr, base, cols, tid, v, p.m, inv);
   }
 }
