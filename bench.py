@@ -502,7 +502,8 @@ def main() -> int:
     ap.add_argument("--secondary", type=int, default=3, help="second workload timed beside it (0: none)")
     ap.add_argument("--no-all-configs", action="store_true", help="skip timing the other workloads")
     ap.add_argument("--no-sclk", action="store_true", help="skip sampling the shader clock")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target oracle time for cpu_baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=14.0,
+                    help="target oracle time for cpu_baseline (the sizing from short runs lands near 70%% of it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
     ap.add_argument("--launches", type=int, default=3)

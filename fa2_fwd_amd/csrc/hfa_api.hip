@@ -26,14 +26,19 @@ using namespace hfa::api;
 #ifndef HFA_BF16_D64_TILE
 #define HFA_BF16_D64_TILE 1, 8
 #endif
-// fp32, d = 64: 256-row workgroups (two 16-query blocks per wave, 8 waves)
-// where the grid still fills every CU, 128-row ones (one block per wave)
-// otherwise.
+// fp32, d = 64: the largest of three tilings whose grid still gives every CU
+// a workgroup -- 256 rows (two 16-query blocks per wave, 8 waves), 128 rows
+// (one block per wave, 8 waves) -- and 64-row workgroups (4 waves) for shapes
+// too small to fill the CUs even so, where more workgroups mean more of the
+// chip at work.
 #ifndef HFA_F32_D64_BIG_TILE
 #define HFA_F32_D64_BIG_TILE 2, 8, 64
 #endif
 #ifndef HFA_F32_D64_SMALL_TILE
 #define HFA_F32_D64_SMALL_TILE 1, 8, 64
+#endif
+#ifndef HFA_F32_D64_TINY_TILE
+#define HFA_F32_D64_TINY_TILE 1, 4, 64
 #endif
 #ifndef HFA_F32_D128_TILE
 #define HFA_F32_D128_TILE 2, 4, 32
@@ -42,16 +47,20 @@ using Bf16D128 = Bf16Tile<128, HFA_BF16_D128_TILE>;
 using Bf16D64 = Bf16Tile<64, HFA_BF16_D64_TILE>;
 using F32D64Big = F32Tile<64, HFA_F32_D64_BIG_TILE>;
 using F32D64Small = F32Tile<64, HFA_F32_D64_SMALL_TILE>;
+using F32D64Tiny = F32Tile<64, HFA_F32_D64_TINY_TILE>;
 using F32D128 = F32Tile<128, HFA_F32_D128_TILE>;
 
 constexpr double kLog2e = 1.44269504088896340736;  // 1 / ln 2
 constexpr int64_t kComputeUnits = 256;  // gfx950 (MI350 series): 8 XCDs x 32 CUs
 
-// Whether the fp32, d = 64 shape takes the 256-row tiling: it does when that
-// grid still gives every compute unit a workgroup.
-bool f32_d64_big(int64_t BH, int64_t N) {
-  const int64_t wgs = BH * ((N + F32D64Big::BR - 1) / F32D64Big::BR);
-  return wgs >= kComputeUnits;
+// Whether a grid of B_r-row workgroups gives every compute unit one.
+bool fills_cus(int64_t BH, int64_t N, int64_t br) { return BH * ((N + br - 1) / br) >= kComputeUnits; }
+
+// fp32, d = 64 tiling of a shape: 2 = 256 rows, 1 = 128 rows, 0 = 64 rows.
+int f32_d64_tiling(int64_t BH, int64_t N) {
+  if (fills_cus(BH, N, F32D64Big::BR)) return 2;
+  if (fills_cus(BH, N, F32D64Small::BR)) return 1;
+  return 0;
 }
 
 // Raise the dynamic-LDS limit of a kernel once per process (per device the
@@ -151,8 +160,11 @@ hfa_status dispatch(const void* q, const void* k, const void* v, void* o, float*
     return launch_bf16<Bf16D64>(q, k, v, o, lse, BH, N, scale, st, launch);
   }
   if (d == 64) {
-    if (f32_d64_big(BH, N)) return launch_f32<F32D64Big>(q, k, v, o, lse, BH, N, scale, st, launch);
-    return launch_f32<F32D64Small>(q, k, v, o, lse, BH, N, scale, st, launch);
+    switch (f32_d64_tiling(BH, N)) {
+      case 2: return launch_f32<F32D64Big>(q, k, v, o, lse, BH, N, scale, st, launch);
+      case 1: return launch_f32<F32D64Small>(q, k, v, o, lse, BH, N, scale, st, launch);
+      default: return launch_f32<F32D64Tiny>(q, k, v, o, lse, BH, N, scale, st, launch);
+    }
   }
   return launch_f32<F32D128>(q, k, v, o, lse, BH, N, scale, st, launch);
 }
@@ -171,7 +183,10 @@ int64_t hfa_block_rows(hfa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t
   if (B < 1 || H < 1 || N < 1 || B > INT64_MAX / H) return 0;
   if (dtype == HFA_BF16 && d == 128) return Bf16D128::BR;
   if (dtype == HFA_BF16 && d == 64) return Bf16D64::BR;
-  if (dtype == HFA_F32 && d == 64) return f32_d64_big(B * H, N) ? F32D64Big::BR : F32D64Small::BR;
+  if (dtype == HFA_F32 && d == 64) {
+    const int t = f32_d64_tiling(B * H, N);
+    return t == 2 ? F32D64Big::BR : t == 1 ? F32D64Small::BR : F32D64Tiny::BR;
+  }
   if (dtype == HFA_F32 && d == 128) return F32D128::BR;
   return 0;
 }

@@ -76,13 +76,16 @@ def test_block_rows_table():
 
 
 def test_block_rows_follow_the_shape():
-    # fp32 d=64 takes 256-row workgroups only when they still cover 256 CUs:
-    # B*H*ceil(N/256) >= 256 (the N=2048, B*H=32 workload), else 128 rows.
+    # fp32 d=64 takes the largest workgroup whose grid still covers 256 CUs:
+    # 256 rows when B*H*ceil(N/256) >= 256 (the N=2048, B*H=32 workload), else
+    # 128 rows when B*H*ceil(N/128) >= 256 (the N=1024 workload), else 64.
     assert hfa.hfa_block_rows(hfa.HFA_F32, 4, 8, 2048, 64) == 256
     assert hfa.hfa_block_rows(hfa.HFA_F32, 4, 8, 1024, 64) == 128
-    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 1, 128, 64) == 128
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 1, 128, 64) == 64
     assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 256, 200, 64) == 256
     assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 255, 256, 64) == 128
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 16, 1024, 64) == 64
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 8, 4096, 64) == 128
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -119,6 +119,15 @@ def test_long_ragged_sequence(dtype, d):
     check_case(f"ragged {dtype} N={N} d={d}", q, k, v, 1.0 / math.sqrt(d), dtype, rows=rows)
 
 
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_very_long_sequence(dtype, d):
+    # 2^18 + 1 keys: 4097 key tiles, one ragged; rows sampled across every query tile range.
+    N = (1 << 18) + 1
+    q, k, v = W.make_inputs(1, 1, N, d, dtype, seed=262145 + d)
+    rows = np.unique(np.r_[0, 1, N // 2, N - 2, N - 1, W.sample_rows(N, 19, seed=d)])
+    check_case(f"very long {dtype} N={N} d={d}", q, k, v, 1.0 / math.sqrt(d), dtype, rows=rows)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_peaked_rows(dtype):
     # Q and K x8: score standard deviation ~ 64 * scale; stresses the rescale.
@@ -126,10 +135,11 @@ def test_peaked_rows(dtype):
     check_case(f"peaked {dtype}", q, k, v, 0.125, dtype)
 
 
-@pytest.mark.parametrize("B,H,N", [(1, 256, 200), (2, 64, 300), (1, 255, 256), (1, 4, 777)])
-def test_f32_d64_both_tilings(B, H, N):
-    # fp32 d=64 takes 256-row workgroups when B*H*ceil(N/256) >= 256, else
-    # 128-row ones; both, with ragged N.
+@pytest.mark.parametrize("B,H,N", [(1, 256, 200), (2, 64, 300), (1, 255, 256), (1, 4, 777), (1, 8, 4000),
+                                   (1, 16, 1000), (1, 1, 65)])
+def test_f32_d64_all_tilings(B, H, N):
+    # fp32 d=64 takes 256-row workgroups when B*H*ceil(N/256) >= 256, 128-row
+    # ones when B*H*ceil(N/128) >= 256, else 64-row ones; all three, ragged N.
     br = hfa.hfa_block_rows(hfa.HFA_F32, B, H, N, 64)
     q, k, v = W.make_inputs(B, H, N, 64, "f32", seed=B * 1000 + H + N, qk_mult=2.0)
     rows = W.sample_rows(N, 24, seed=N)
