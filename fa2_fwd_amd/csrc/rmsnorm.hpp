@@ -13,8 +13,9 @@
 // ITEMS slots of 16 bytes of the row in registers, so x and the residual are
 // read once: the sum of squares is reduced over the group (wave shuffles, then
 // LDS across the group's waves) and the same registers are normalised and
-// written (16-byte outputs with non-temporal stores: nothing reads them back
-// here).  Element i of a row is read and written by one thread, and all its
+// written (16-byte accesses to x, the residual and the outputs are
+// non-temporal: each is touched once; the weight row, read by every row,
+// stays cacheable).  Element i of a row is read and written by one thread, and all its
 // reads precede its writes, so y and s may be written over x or the residual.
 #pragma once
 
@@ -31,8 +32,9 @@ struct RmsElt<float> {
   static constexpr int kPerSlot = 4;  // elements per 16-byte slot
   __device__ static float load(const float* p) { return *p; }
   __device__ static void store(float* p, float v) { *p = v; }
+  template <bool NT = false>
   __device__ static void load_slot(const float* p, float (&v)[4]) {
-    const f32x4 q = load16<false>(reinterpret_cast<const f32x4*>(p));
+    const f32x4 q = load16<NT>(reinterpret_cast<const f32x4*>(p));
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = q[e];
   }
@@ -46,8 +48,9 @@ struct RmsElt<__bf16> {
   static constexpr int kPerSlot = 8;
   __device__ static float load(const __bf16* p) { return static_cast<float>(*p); }
   __device__ static void store(__bf16* p, float v) { *p = static_cast<__bf16>(v); }
+  template <bool NT = false>
   __device__ static void load_slot(const __bf16* p, float (&v)[8]) {
-    const bf16x8 q = load16<false>(reinterpret_cast<const bf16x8*>(p));
+    const bf16x8 q = load16<NT>(reinterpret_cast<const bf16x8*>(p));
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = static_cast<float>(q[e]);
   }
@@ -105,10 +108,10 @@ __global__ __launch_bounds__(NT) void rmsnorm_kernel(const T* x, const T* res, c
     if (VEC) {
       const int c0 = rms_col<G, PER, true>(s, t, 0);
       if (live && c0 < cols) {
-        E::load_slot(xr + c0, v[s]);
+        E::template load_slot<true>(xr + c0, v[s]);
         if (HAS_RES) {
           float r[PER];
-          E::load_slot(rr + c0, r);
+          E::template load_slot<true>(rr + c0, r);
 #pragma unroll
           for (int e = 0; e < PER; ++e) v[s][e] += r[e];
         }

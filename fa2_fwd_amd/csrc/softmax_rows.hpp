@@ -17,7 +17,7 @@
 //    non-temporal loads.
 //  * Streaming path: the thread's running pair is updated chunk by chunk
 //    while x streams through (UNROLL 16-byte loads in flight per thread), then
-//    x is read a second time to write y.
+//    x is read a second time, last chunk first, to write y.
 //
 // y is written with non-temporal stores.  Exponentials are exp2 of
 // (x - M) * log2(e), the difference taken first so that large |x| loses no
@@ -165,7 +165,9 @@ __global__ __launch_bounds__(NT) void softmax_rows_stream_kernel(const float* x,
   }
   p = merge_workgroup<NT>(p, lds);
   const float inv = 1.0f / p.l;
-  for (int64_t base = 0; base < cols; base += STEP) {
+  // The second pass walks the row backwards: the chunks read last by the
+  // first pass are the likeliest still to be held by the caches.
+  for (int64_t base = (cols - 1) / STEP * STEP; base >= 0; base -= STEP) {
     float v[UNROLL * 4];
     load_slots<NT, VEC, UNROLL, false>(xr, base, cols, tid, v);
     store_slots<NT, VEC, UNROLL>(yr, base, cols, tid, v, p.m, inv);
