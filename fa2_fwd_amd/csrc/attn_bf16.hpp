@@ -51,9 +51,6 @@ namespace hfa {
 #ifndef HFA_NBUF
 #define HFA_NBUF 4
 #endif
-#ifndef HFA_DOT2_SUM
-#define HFA_DOT2_SUM 0
-#endif
 
 template <int D_, int QB_, int NW_>
 struct Bf16Tile {
@@ -463,20 +460,6 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
         for (int c = 0; c < KT / 16; ++c)
 #pragma unroll
           for (int e = 0; e < 8; ++e) pf[qb][c][e] = static_cast<__bf16>(pv[8 * c + e]);
-#if HFA_DOT2_SUM
-        // the sum of the bf16-rounded weights (the ones that multiply V), two
-        // per v_dot2c_f32_bf16 against (1, 1), in four independent chains
-        const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-        float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int c = 0; c < KT / 16; ++c)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const bf16x2 pair = {pf[qb][c][2 * e], pf[qb][c][2 * e + 1]};
-            part[e] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, part[e], false);
-          }
-        return (part[0] + part[1]) + (part[2] + part[3]);
-#else
         float part[NS / 4];
 #pragma unroll
         for (int u = 0; u < NS / 4; ++u) part[u] = (pv[4 * u] + pv[4 * u + 1]) + (pv[4 * u + 2] + pv[4 * u + 3]);
@@ -485,7 +468,6 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
 #pragma unroll
           for (int u = 0; u < w; ++u) part[u] += part[u + w];
         return part[0];
-#endif
       };
       float tsum;
       if constexpr (first || !HFA_LAZY_MAX) {
