@@ -53,3 +53,39 @@ def test_graph_on_a_side_stream():
         g.launch(stream=side)
         side.synchronize()
         assert torch.equal(g.out, o_ref) and torch.equal(g.lse, lse_ref)
+
+
+def test_softmax_and_rmsnorm_under_torch_graph_capture():
+    # The HBM-bound entry points launch kernels only (no memset, no allocation),
+    # so a caller can capture them into a graph: every replay must equal the
+    # eager result, with unrelated eager work and fills between replays.
+    dev = torch.device("cuda:0")
+    g = torch.Generator("cpu").manual_seed(21)
+    xs = (torch.randn(64, 70001, generator=g) * 4.0).to(dev)  # streaming softmax path, ragged width
+    xs2 = (torch.randn(128, 3000, generator=g) * 4.0).to(dev)  # register-resident path
+    rw = W.RmsNormWorkload("graph", 300, 4096, "bf16", 22)
+    xr, rr, wr = (t.to(dev) for t in rw.inputs())
+    ys, ys2 = torch.empty_like(xs), torch.empty_like(xs2)
+    yr, sr = torch.empty_like(xr), torch.empty_like(xr)
+    ref = (hfa.softmax_rows(xs), hfa.softmax_rows(xs2), *hfa.rmsnorm(xr, wr, rw.eps, residual=rr))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):  # warm-up on the capture stream, as torch's graph docs ask
+        hfa.softmax_rows(xs, out=ys)
+    side.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        hfa.softmax_rows(xs, out=ys)
+        hfa.softmax_rows(xs2, out=ys2)
+        hfa.rmsnorm(xr, wr, rw.eps, residual=rr, out=yr, residual_out=sr)
+    for rep in range(3):
+        for t in (ys, ys2, yr, sr):
+            t.fill_(float("nan"))
+        hfa.softmax_rows(xs2 * 0.5)  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ys, ref[0]) and torch.equal(ys2, ref[1]), f"replay {rep}: softmax differs"
+        assert torch.equal(yr.view(torch.int16), ref[2].view(torch.int16)), f"replay {rep}: rmsnorm y differs"
+        assert torch.equal(sr.view(torch.int16), ref[3].view(torch.int16)), f"replay {rep}: rmsnorm sum differs"
