@@ -303,6 +303,27 @@ def hbm_op_cpu_baseline(op: str, wl, target_s: float):
             "sample": f"{n} of {wl.rows} rows (evenly spaced), {what}; {t:.2f} s"}
 
 
+def device_copy_gbs(nbytes: int = 1 << 30, reps: int = 20) -> float:
+    """Context for the HBM roof: GB/s (bytes read + written) of torch's own device copy."""
+    import torch
+
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    log(f"[bench] torch device copy of {nbytes >> 20} MiB: {gbs:.0f} GB/s (read + write)")
+    return round(gbs, 1)
+
+
 def _sclk_files():
     return sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
 
@@ -590,6 +611,7 @@ def main() -> int:
     sclk = None if args.no_sclk else observed_sclk(w, 0.5)
     if sclk is not None:
         log(f"[bench] shader clock during {w.describe()}: {sclk:.0f} MHz (median of sysfs samples)")
+    copy_gbs = None if (args.no_softmax and args.no_rmsnorm) else device_copy_gbs()
     hbm = {}
     for op, skip, baseline_cfg in (("softmax", args.no_softmax, 1), ("rmsnorm", args.no_rmsnorm, 3)):
         if skip:
@@ -626,6 +648,7 @@ def main() -> int:
         "all_configs": all_configs,
         "softmax_rows": hbm.get("softmax_rows"),
         "rmsnorm": hbm.get("rmsnorm"),
+        "device_copy_gbs": copy_gbs,
         "observed_sclk_mhz": sclk,
         "device": getattr(props, "gcnArchName", props.name),
     }
