@@ -110,6 +110,10 @@ constexpr float kRescaleLog2 = 8.0f;
 // Largest lane sum of one tile's weights accepted without forming the max.
 constexpr float kSumLimit = 65536.0f;
 
+#ifndef HFA_RING_UNROLL
+#define HFA_RING_UNROLL 1
+#endif
+
 #ifndef HFA_MFMA_PRIO
 #define HFA_MFMA_PRIO 1
 #endif
@@ -264,9 +268,18 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
     const int ch = phys ^ (grp == 0 ? k_swz<T::CH>(row) : v_swz<T::CH>(row));
     dma_off[u] = (row * D + ch * 8) * 2;
   }
-  auto issue_tile = [&](int t) {
+  // Ring slot of tile t: t % NBUF, or a compile-time constant equal to it
+  // (the unrolled loop below passes one, so slot addresses fold into the
+  // immediate offsets of the LDS instructions).
+  auto slot_of = [&](int t, auto slot) __attribute__((always_inline)) -> int {
+    if constexpr (std::is_integral_v<decltype(slot)>)
+      return t % T::NBUF;
+    else
+      return decltype(slot)::value;
+  };
+  auto issue_tile = [&](int t, auto slot) __attribute__((always_inline)) {
     if (t >= ntiles) return;
-    char* dst = stream_ring + (t % T::NBUF) * TILEB;
+    char* dst = stream_ring + slot_of(t, slot) * TILEB;
     const char* tile_src = reinterpret_cast<const char*>(stream_src + static_cast<size_t>(t) * KT * D);
     if ((t + 1) * KT <= N) {
 #pragma unroll
@@ -317,33 +330,35 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   // operands only: V tiles are published one interval later (see the waits).
   static_assert(PF <= SSTEPS, "only score operands are read ahead of the MFMA phase");
   u32x4 opnd[PF + 1];
-  auto load_op = [&](int i, bool with_pv, const char* kt, const char* vt) -> u32x4 {
+  auto load_op = [&](int i, bool with_pv, const char* kt, const char* vt) __attribute__((always_inline)) -> u32x4 {
     const int st = op_step(i, with_pv);
     if (op_is_score(i, with_pv)) return lds_load16(kt, k_off(st));
     const s16x4 lo = lds_read_tr16(vt, v_off(st));
     const s16x4 hi = lds_read_tr16(vt, v_off(st) + 4 * ROWB);
     return __builtin_bit_cast(u32x4, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   };
-  auto prefetch_operands = [&](int j, auto with_pv_tag) {  // first PF operations of MFMA phase j
+  auto prefetch_operands = [&](int j, auto with_pv_tag, auto slot) __attribute__((always_inline)) {  // first PF operations of MFMA phase j
     constexpr bool with_pv = decltype(with_pv_tag)::value;
-    const char* kt = kbuf + (j % T::NBUF) * TILEB;
-    const char* vt = vbuf + ((j + T::NBUF - 1) % T::NBUF) * TILEB;
+    const int sj = slot_of(j, slot);
+    const char* kt = kbuf + sj * TILEB;
+    const char* vt = vbuf + ((sj + T::NBUF - 1) % T::NBUF) * TILEB;
 #pragma unroll
     for (int i = 0; i < PF; ++i) opnd[i] = load_op(i, with_pv, kt, vt);
   };
-  auto mfma_phase = [&](int j, auto with_pv_tag, auto prefetched_tag) {
+  auto mfma_phase = [&](int j, auto with_pv_tag, auto prefetched_tag, auto slot) __attribute__((always_inline)) {
     constexpr bool with_pv = decltype(with_pv_tag)::value;
     constexpr bool prefetched = decltype(prefetched_tag)::value;
     constexpr int nops = with_pv ? NOPS : SSTEPS;
-    const char* kt = kbuf + (j % T::NBUF) * TILEB;
-    const char* vt = vbuf + ((j + T::NBUF - 1) % T::NBUF) * TILEB;
+    const int sj = slot_of(j, slot);
+    const char* kt = kbuf + sj * TILEB;
+    const char* vt = vbuf + ((sj + T::NBUF - 1) % T::NBUF) * TILEB;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int kb = 0; kb < KT / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.0f;
-    if (!prefetched) prefetch_operands(j, with_pv_tag);
+    if (!prefetched) prefetch_operands(j, with_pv_tag, slot);
 #pragma unroll
     for (int i = 0; i < nops; ++i) {
       if (i + PF < nops) opnd[(i + PF) % (PF + 1)] = load_op(i + PF, with_pv, kt, vt);
@@ -392,7 +407,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
 #endif
   };
   // final output product of the last tile, without scores
-  auto mfma_pv_only = [&](int j) {
+  auto mfma_pv_only = [&](int j) __attribute__((always_inline)) {
     const char* vt = vbuf + (j % T::NBUF) * TILEB;
 #pragma unroll
     for (int i = 0; i < STEPS; ++i) {
@@ -419,7 +434,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   // kSumLimit / (KT/2) = 2^11, a growth beyond kRescaleLog2, and only then is
   // the row max of x formed, the rescale applied and the weights redone (a
   // rare, wave-uniform branch).  Every weight stays <= kSumLimit either way.
-  auto softmax = [&](int j, auto first_tag) {
+  auto softmax = [&](int j, auto first_tag) __attribute__((always_inline)) {
     constexpr bool first = decltype(first_tag)::value;
     const int key0 = j * KT;
     if (key0 + KT > N) {  // keys past the end of the sequence get score -inf (weight 0)
@@ -531,7 +546,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   // Wait until this group's request for tile t is complete.  Requests go
   // out in tile order and only for tiles < ntiles, so the number that may
   // still be in flight is LD times the number of tiles requested after t.
-  auto wait_tile = [&](int t, int newest) {
+  auto wait_tile = [&](int t, int newest) __attribute__((always_inline)) {
     const int after = min(newest, ntiles - 1) - t;
     static_assert(T::AHEAD <= 4, "wait counts are spelled out up to three newer tiles");
     if (after <= 0)
@@ -547,7 +562,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   // ---- prologue: the first AHEAD tiles of each stream; K_0 (group 0) must
   // be complete before the first barrier.
 #pragma unroll
-  for (int t = 0; t < T::AHEAD; ++t) issue_tile(t);
+  for (int t = 0; t < T::AHEAD; ++t) issue_tile(t, 0);
   if (grp == 0) wait_tile(0, T::AHEAD - 1);
   lds_barrier();
   if (grp == 1) lds_barrier();  // group 1 runs half a tile behind
@@ -561,31 +576,50 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   // HBM request for tile j + AHEAD of this group's stream and the softmax of
   // tile j.  Tile 0 is peeled off so that the accumulator flows straight
   // through the loop body.
-  auto close_mfma_phase = [&](int j) {
+  auto close_mfma_phase = [&](int j) __attribute__((always_inline)) {
     if (grp == 0)
       wait_tile(j + 1, j - 1 + T::AHEAD);
     else
       wait_tile(j, j - 1 + T::AHEAD);
     lds_barrier();
   };
-  auto valu_phase = [&](int j, auto first_tag) {
-    if (j + 1 < ntiles) prefetch_operands(j + 1, std::true_type{});
-    issue_tile(j + T::AHEAD);
+  auto next_slot = [&](auto slot, auto step) __attribute__((always_inline)) {
+    if constexpr (std::is_integral_v<decltype(slot)>)
+      return slot;
+    else
+      return std::integral_constant<int, (decltype(slot)::value + decltype(step)::value) % T::NBUF>{};
+  };
+  auto valu_phase = [&](int j, auto first_tag, auto slot) __attribute__((always_inline)) {
+    if (j + 1 < ntiles) prefetch_operands(j + 1, std::true_type{}, next_slot(slot, std::integral_constant<int, 1>{}));
+    issue_tile(j + T::AHEAD, next_slot(slot, std::integral_constant<int, T::AHEAD>{}));
     softmax(j, first_tag);
     lds_barrier();
   };
-  wave_prio(true);
-  mfma_phase(0, std::false_type{}, std::false_type{});
-  wave_prio(false);
-  close_mfma_phase(0);
-  valu_phase(0, std::true_type{});
-  for (int j = 1; j < ntiles; ++j) {
+  auto step = [&](int j, auto slot) __attribute__((always_inline)) {
     wave_prio(true);
-    mfma_phase(j, std::true_type{}, std::true_type{});
+    mfma_phase(j, std::true_type{}, std::true_type{}, slot);
     wave_prio(false);
     close_mfma_phase(j);
-    valu_phase(j, std::false_type{});
+    valu_phase(j, std::false_type{}, slot);
+  };
+  wave_prio(true);
+  mfma_phase(0, std::false_type{}, std::false_type{}, 0);
+  wave_prio(false);
+  close_mfma_phase(0);
+  valu_phase(0, std::true_type{}, 0);
+  int j = 1;
+#if HFA_RING_UNROLL
+  // NBUF tiles per trip with the ring slot of each known at compile time
+  // (j % NBUF == 1 at the top of a trip).
+  static_assert(T::NBUF == 4, "the unrolled trip is written for a 4-slot ring");
+  for (; j + 3 < ntiles; j += 4) {
+    step(j, std::integral_constant<int, 1>{});
+    step(j + 1, std::integral_constant<int, 2>{});
+    step(j + 2, std::integral_constant<int, 3>{});
+    step(j + 3, std::integral_constant<int, 0>{});
   }
+#endif
+  for (; j < ntiles; ++j) step(j, 0);
   wave_prio(true);
   mfma_pv_only(ntiles - 1);
   wave_prio(false);
