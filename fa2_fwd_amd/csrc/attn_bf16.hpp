@@ -312,9 +312,14 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
     const int kb = i % (KT / 32), t = i / (KT / 32);
     return (kb * 32 + krow) * ROWB + (((2 * t + hh) ^ kswz) << 4);
   };
+  // The lane-dependent part of each column block's V address, formed once:
+  // the key chunk and the ring slot then only add constants.
+  int vlane[D / 32];
+#pragma unroll
+  for (int n = 0; n < D / 32; ++n) vlane[n] = vrow * ROWB + (((4 * n + vch) ^ vswz) << 4) + vin;
   auto v_off = [&](int i) {  // step i: column block i % (D/32), key chunk i / (D/32)
     const int n = i % (D / 32), c = i / (D / 32);
-    return (16 * c + vrow) * ROWB + (((4 * n + vch) ^ vswz) << 4) + vin;
+    return vlane[n] + 16 * c * ROWB;
   };
   // The MFMA phase is a sequence of operations, each one MFMA with its LDS
   // operand: the SSTEPS score MFMAs first (so the scores are complete, and
