@@ -277,11 +277,13 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
     else
       return decltype(slot)::value;
   };
-  auto issue_tile = [&](int t, auto slot) __attribute__((always_inline)) {
-    if (t >= ntiles) return;
+  // steady: the caller guarantees t < ntiles - 1 (a full tile that exists).
+  auto issue_tile = [&](int t, auto slot, auto steady_tag) __attribute__((always_inline)) {
+    constexpr bool steady = decltype(steady_tag)::value;
+    if (!steady && t >= ntiles) return;
     char* dst = stream_ring + slot_of(t, slot) * TILEB;
     const char* tile_src = reinterpret_cast<const char*>(stream_src + static_cast<size_t>(t) * KT * D);
-    if ((t + 1) * KT <= N) {
+    if (steady || (t + 1) * KT <= N) {
 #pragma unroll
       for (int u = 0; u < T::LD; ++u) dma16(tile_src, dma_off[u], dst + (wig * T::LD + u) * 1024);
     } else {  // ragged last tile: rows past the end re-read the last row
@@ -439,10 +441,11 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   // kSumLimit / (KT/2) = 2^11, a growth beyond kRescaleLog2, and only then is
   // the row max of x formed, the rescale applied and the weights redone (a
   // rare, wave-uniform branch).  Every weight stays <= kSumLimit either way.
-  auto softmax = [&](int j, auto first_tag) __attribute__((always_inline)) {
+  auto softmax = [&](int j, auto first_tag, auto steady_tag) __attribute__((always_inline)) {
     constexpr bool first = decltype(first_tag)::value;
+    constexpr bool steady = decltype(steady_tag)::value;  // tile j is not the last: no key past N
     const int key0 = j * KT;
-    if (key0 + KT > N) {  // keys past the end of the sequence get score -inf (weight 0)
+    if (!steady && key0 + KT > N) {  // keys past the end of the sequence get score -inf (weight 0)
 #pragma unroll
       for (int kb = 0; kb < KT / 32; ++kb)
 #pragma unroll
@@ -567,7 +570,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   // ---- prologue: the first AHEAD tiles of each stream; K_0 (group 0) must
   // be complete before the first barrier.
 #pragma unroll
-  for (int t = 0; t < T::AHEAD; ++t) issue_tile(t, 0);
+  for (int t = 0; t < T::AHEAD; ++t) issue_tile(t, 0, std::false_type{});
   if (grp == 0) wait_tile(0, T::AHEAD - 1);
   lds_barrier();
   if (grp == 1) lds_barrier();  // group 1 runs half a tile behind
@@ -581,11 +584,21 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   // HBM request for tile j + AHEAD of this group's stream and the softmax of
   // tile j.  Tile 0 is peeled off so that the accumulator flows straight
   // through the loop body.
-  auto close_mfma_phase = [&](int j) __attribute__((always_inline)) {
-    if (grp == 0)
-      wait_tile(j + 1, j - 1 + T::AHEAD);
-    else
-      wait_tile(j, j - 1 + T::AHEAD);
+  // steady: tiles j - 1 + AHEAD and j + AHEAD exist and are not the last, so
+  // the wait counts are fixed and no request needs a bounds or ragged check.
+  auto close_mfma_phase = [&](int j, auto steady_tag) __attribute__((always_inline)) {
+    constexpr bool steady = decltype(steady_tag)::value;
+    if constexpr (steady) {
+      if (grp == 0)
+        vmcnt_wait<(T::AHEAD - 2) * T::LD>();
+      else
+        vmcnt_wait<(T::AHEAD - 1) * T::LD>();
+    } else {
+      if (grp == 0)
+        wait_tile(j + 1, j - 1 + T::AHEAD);
+      else
+        wait_tile(j, j - 1 + T::AHEAD);
+    }
     lds_barrier();
   };
   auto next_slot = [&](auto slot, auto step) __attribute__((always_inline)) {
@@ -594,37 +607,41 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
     else
       return std::integral_constant<int, (decltype(slot)::value + decltype(step)::value) % T::NBUF>{};
   };
-  auto valu_phase = [&](int j, auto first_tag, auto slot) __attribute__((always_inline)) {
-    if (j + 1 < ntiles) prefetch_operands(j + 1, std::true_type{}, next_slot(slot, std::integral_constant<int, 1>{}));
-    issue_tile(j + T::AHEAD, next_slot(slot, std::integral_constant<int, T::AHEAD>{}));
-    softmax(j, first_tag);
+  auto valu_phase = [&](int j, auto first_tag, auto slot, auto steady_tag) __attribute__((always_inline)) {
+    constexpr bool steady = decltype(steady_tag)::value;
+    if (steady || j + 1 < ntiles)
+      prefetch_operands(j + 1, std::true_type{}, next_slot(slot, std::integral_constant<int, 1>{}));
+    issue_tile(j + T::AHEAD, next_slot(slot, std::integral_constant<int, T::AHEAD>{}), steady_tag);
+    softmax(j, first_tag, steady_tag);
     lds_barrier();
   };
-  auto step = [&](int j, auto slot) __attribute__((always_inline)) {
+  auto step = [&](int j, auto slot, auto steady_tag) __attribute__((always_inline)) {
     wave_prio(true);
     mfma_phase(j, std::true_type{}, std::true_type{}, slot);
     wave_prio(false);
-    close_mfma_phase(j);
-    valu_phase(j, std::false_type{}, slot);
+    close_mfma_phase(j, steady_tag);
+    valu_phase(j, std::false_type{}, slot, steady_tag);
   };
   wave_prio(true);
   mfma_phase(0, std::false_type{}, std::false_type{}, 0);
   wave_prio(false);
-  close_mfma_phase(0);
-  valu_phase(0, std::true_type{}, 0);
+  close_mfma_phase(0, std::false_type{});
+  valu_phase(0, std::true_type{}, 0, std::false_type{});
   int j = 1;
 #if HFA_RING_UNROLL
   // NBUF tiles per trip with the ring slot of each known at compile time
-  // (j % NBUF == 1 at the top of a trip).
-  static_assert(T::NBUF == 4, "the unrolled trip is written for a 4-slot ring");
-  for (; j + 3 < ntiles; j += 4) {
-    step(j, std::integral_constant<int, 1>{});
-    step(j + 1, std::integral_constant<int, 2>{});
-    step(j + 2, std::integral_constant<int, 3>{});
-    step(j + 3, std::integral_constant<int, 0>{});
+  // (j % NBUF == 1 at the top of a trip).  A trip runs only while every step
+  // in it is steady: its last step, j + 3, requests tile j + 3 + AHEAD, which
+  // must be below ntiles - 1.
+  static_assert(T::NBUF == 4 && T::AHEAD == 3, "the unrolled trip is written for a 4-slot ring");
+  for (; j + 3 + T::AHEAD < ntiles - 1; j += 4) {
+    step(j, std::integral_constant<int, 1>{}, std::true_type{});
+    step(j + 1, std::integral_constant<int, 2>{}, std::true_type{});
+    step(j + 2, std::integral_constant<int, 3>{}, std::true_type{});
+    step(j + 3, std::integral_constant<int, 0>{}, std::true_type{});
   }
 #endif
-  for (; j < ntiles; ++j) step(j, 0);
+  for (; j < ntiles; ++j) step(j, 0, std::false_type{});
   wave_prio(true);
   mfma_pv_only(ntiles - 1);
   wave_prio(false);
