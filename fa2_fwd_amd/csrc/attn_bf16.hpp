@@ -586,9 +586,14 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   // through the loop body.
   // steady: tiles j - 1 + AHEAD and j + AHEAD exist and are not the last, so
   // the wait counts are fixed and no request needs a bounds or ragged check.
-  auto close_mfma_phase = [&](int j, auto steady_tag) __attribute__((always_inline)) {
+  auto close_mfma_phase = [&](int j, auto steady_tag, auto grp_tag) __attribute__((always_inline)) {
     constexpr bool steady = decltype(steady_tag)::value;
-    if constexpr (steady) {
+    constexpr int g = decltype(grp_tag)::value;  // -1: read the group at run time
+    if constexpr (steady && g == 0) {
+      vmcnt_wait<(T::AHEAD - 2) * T::LD>();
+    } else if constexpr (steady && g == 1) {
+      vmcnt_wait<(T::AHEAD - 1) * T::LD>();
+    } else if constexpr (steady) {
       if (grp == 0)
         vmcnt_wait<(T::AHEAD - 2) * T::LD>();
       else
@@ -615,17 +620,18 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
     softmax(j, first_tag, steady_tag);
     lds_barrier();
   };
-  auto step = [&](int j, auto slot, auto steady_tag) __attribute__((always_inline)) {
+  auto step = [&](int j, auto slot, auto steady_tag, auto grp_tag) __attribute__((always_inline)) {
     wave_prio(true);
     mfma_phase(j, std::true_type{}, std::true_type{}, slot);
     wave_prio(false);
-    close_mfma_phase(j, steady_tag);
+    close_mfma_phase(j, steady_tag, grp_tag);
     valu_phase(j, std::false_type{}, slot, steady_tag);
   };
+  using RtGrp = std::integral_constant<int, -1>;
   wave_prio(true);
   mfma_phase(0, std::false_type{}, std::false_type{}, 0);
   wave_prio(false);
-  close_mfma_phase(0, std::false_type{});
+  close_mfma_phase(0, std::false_type{}, RtGrp{});
   valu_phase(0, std::true_type{}, 0, std::false_type{});
   int j = 1;
 #if HFA_RING_UNROLL
@@ -634,14 +640,22 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   // in it is steady: its last step, j + 3, requests tile j + 3 + AHEAD, which
   // must be below ntiles - 1.
   static_assert(T::NBUF == 4 && T::AHEAD == 3, "the unrolled trip is written for a 4-slot ring");
-  for (; j + 3 + T::AHEAD < ntiles - 1; j += 4) {
-    step(j, std::integral_constant<int, 1>{}, std::true_type{});
-    step(j + 1, std::integral_constant<int, 2>{}, std::true_type{});
-    step(j + 2, std::integral_constant<int, 3>{}, std::true_type{});
-    step(j + 3, std::integral_constant<int, 0>{}, std::true_type{});
-  }
+  auto trips = [&](auto grp_tag) __attribute__((always_inline)) {
+    for (; j + 3 + T::AHEAD < ntiles - 1; j += 4) {
+      step(j, std::integral_constant<int, 1>{}, std::true_type{}, grp_tag);
+      step(j + 1, std::integral_constant<int, 2>{}, std::true_type{}, grp_tag);
+      step(j + 2, std::integral_constant<int, 3>{}, std::true_type{}, grp_tag);
+      step(j + 3, std::integral_constant<int, 0>{}, std::true_type{}, grp_tag);
+    }
+  };
+  // One copy of the trips per group, so the group's wait count is an
+  // immediate rather than a branch in every phase.
+  if (grp == 0)
+    trips(std::integral_constant<int, 0>{});
+  else
+    trips(std::integral_constant<int, 1>{});
 #endif
-  for (; j < ntiles; ++j) step(j, 0, std::false_type{});
+  for (; j < ntiles; ++j) step(j, 0, std::false_type{}, RtGrp{});
   wave_prio(true);
   mfma_pv_only(ntiles - 1);
   wave_prio(false);
