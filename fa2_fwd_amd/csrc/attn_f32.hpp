@@ -27,6 +27,8 @@
 // output columns of its own query, so the rescale is lane-local.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace hfa {
@@ -128,14 +130,16 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
   }
 
   u32x4 kreg[T::LOADS], vreg[T::LOADS];
-  auto stage_load = [&](int j) {
+  // full: tile j lies wholly below N (no key needs the bounds check).
+  auto stage_load = [&](int j, auto full_tag) __attribute__((always_inline)) {
+    constexpr bool full = decltype(full_tag)::value;
 #pragma unroll
     for (int u = 0; u < T::LOADS; ++u) {
       const int idx = tid + u * T::NT;
       const int row = idx / T::CH, ch = idx % T::CH;
       const int key = j * KT + row;
       u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-      if (key < N) {
+      if (full || key < N) {
         kx = *reinterpret_cast<const u32x4*>(Kh + static_cast<size_t>(key) * D + ch * 4);
         vx = *reinterpret_cast<const u32x4*>(Vh + static_cast<size_t>(key) * D + ch * 4);
       }
@@ -143,7 +147,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
       vreg[u] = vx;
     }
   };
-  auto stage_store = [&](int buf) {
+  auto stage_store = [&](int buf) __attribute__((always_inline)) {
     char* kt = smem + buf * (T::KTILEB + T::VTILEB);
     char* vt = kt + T::KTILEB;
 #pragma unroll
@@ -156,13 +160,26 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
   };
 
   const int ntiles = (N + KT - 1) / KT;
-  stage_load(0);
+  stage_load(0, std::false_type{});
   stage_store(0);
   __syncthreads();
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) stage_load(j + 1);
+  // One key tile.  buf is the LDS buffer of tile j (j & 1), a compile-time
+  // constant in the unrolled loop below so that the buffer offset folds into
+  // the LDS instructions; steady: tile j + 1 is wholly below N and tile j is
+  // not the last, so no bounds check, no masking and no end-of-loop test.
+  auto tile_step = [&](int j, auto buf_tag, auto steady_tag) __attribute__((always_inline)) {
+    constexpr bool steady = decltype(steady_tag)::value;
+    const int buf = [&] {
+      if constexpr (std::is_integral_v<decltype(buf_tag)>)
+        return j & 1;
+      else
+        return static_cast<int>(decltype(buf_tag)::value);
+    }();
+    if (steady)
+      stage_load(j + 1, std::true_type{});
+    else if (j + 1 < ntiles)
+      stage_load(j + 1, std::false_type{});
     const char* kt = smem + buf * (T::KTILEB + T::VTILEB);
     const char* vt = kt + T::KTILEB;
 
@@ -191,7 +208,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
 
     // ---- keys past the end get score -inf
     const int key0 = j * KT;
-    if (key0 + KT > N) {
+    if (!steady && key0 + KT > N) {
 #pragma unroll
       for (int kb = 0; kb < KT / 16; ++kb)
 #pragma unroll
@@ -250,9 +267,16 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
       }
     }
 
-    if (j + 1 < ntiles) stage_store(buf ^ 1);
+    if (steady || j + 1 < ntiles) stage_store(buf ^ 1);
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 3 < ntiles; j += 2) {
+    tile_step(j, std::integral_constant<int, 0>{}, std::true_type{});
+    tile_step(j + 1, std::integral_constant<int, 1>{}, std::true_type{});
   }
+  for (; j < ntiles; ++j) tile_step(j, 0, std::false_type{});
+
 
   // ---- epilogue.  acc[qb][n][r] is O[q][64*(n/4) + 16g + 4r + n%4].
 #pragma unroll
