@@ -40,6 +40,13 @@
 // group 1: V_j, read by group 0's next MFMA phase).  Across the barrier
 // intervals a buffer is refilled only after both groups finished reading its
 // previous tile (tests/test_schedule_model.py checks both properties).
+//
+// Loop shape.  While more than NBUF + AHEAD tiles remain, the loop runs
+// "steady" trips of NBUF tiles, one per ring slot, with the slot a
+// compile-time constant (LDS offsets fold into instruction immediates) and
+// no bounds, ragged-tile or masking checks; each group runs its own copy of
+// these trips, so its HBM wait count is an immediate too.  The last tiles
+// go through a general step that checks everything at run time.
 #pragma once
 
 #include <type_traits>
