@@ -6,9 +6,22 @@
 // not accurate enough when rows are peaked (scores of tens of units: the
 // rounding of the running dot product moves exp(s - m) of the dominant keys
 // by more than 1e-5 relative).  So:
-//  * S^T = K Q^T runs on the fp64 matrix cores (v_mfma_f64_16x16x4_f64) from
-//    the exactly widened fp32 inputs: every product is exact and the sums are
-//    fp64.
+//  * S^T = K Q^T is formed exactly (up to one fp64 rounding) on the int8
+//    matrix cores by error-free slicing (the Ozaki scheme: K. Ozaki,
+//    T. Ogita, S. Oishi, S. M. Rump, "Error-free transformations of matrix
+//    multiplication by using fast routines of matrix multiplication and its
+//    applications", Numer. Algorithms 59, 2012; its integer form after
+//    Ootomo, Ozaki and Yokota, "DGEMM on integer matrix multiplication
+//    unit", IJHPCA 2024).  Each row x of Q and of K is written with a power
+//    of two 2^e above its largest magnitude as
+//        x = 2^(e-6) * sum_{a<5} s_a 2^(-7a) + r,   s_a integers, |s_a| <= 64,
+//    with |r| <= 2^(e-35) (zero for every element within 2^-11 of the row
+//    maximum, since fp32 carries 24 significant bits).  The slice products
+//    sum_d s_a(q) s_b(k) are exact in the int32 accumulators; those with
+//    a + b <= 5 are formed (19 of 25; each dropped one is below 2^-40 of
+//    max|q| max|k| per column), grouped by a + b, and combined in fp64.
+//    int8 MFMAs run at 64 times the fp64 rate, so the 19 cost 0.3 of the
+//    fp64 product.
 //  * The running max is kept in the log2 domain and rounded up to an integer
 //    m2, so each rescale factor 2^(m2_old - m2_new) is an exact power of two.
 //  * s * c - m2 is formed in fp64, rounded once to fp32 and exponentiated on
@@ -28,12 +41,13 @@
 //  * The running denominator is accumulated in fp64, and the log-sum-exp is
 //    combined in fp64 and rounded once.
 //
-// Matrix-core mapping.  S^T: A = 16 key rows of K, B = 16 query rows of Q, the
-// contraction index d permuted so that each lane reads d/4 consecutive
-// columns; the f64 accumulator gives lane (q = lane % 16, g = lane / 16)
-// register r the key 4r + g of the 16-key block.  O^T = V^T P^T on
+// Matrix-core mapping.  S^T on v_mfma_i32_16x16x64_i8: A = one slice of 16
+// key rows (64 head-dim columns per instruction, lane group g holding columns
+// 16g .. 16g + 15), B = one slice of 16 query rows in the same column order;
+// the int32 result gives lane (q = lane % 16, g = lane / 16) register r the
+// key 4g + r of the 16-key block.  O^T = V^T P^T on
 // v_mfma_f32_16x16x32_bf16, one 32-key chunk c at a time: the contraction
-// slot 8g + i (i < 8) of lane group g stands for key 16 (i / 4) + 4 (i % 4) + g
+// slot 8g + i (i < 8) of lane group g stands for key 16 (i / 4) + 4 g + i % 4
 // of the chunk, which is exactly the lane's own weight in register i % 4 of
 // score block 2c + i / 4, so the B operand is the lane's own P.  The A operand
 // (V^T, 16 head-dim columns by the same 32 keys) is stored in LDS in that
@@ -57,8 +71,10 @@ struct F32Tile {
   static constexpr int WQ = 16 * QB;  // queries per wave
   static constexpr int BR = WQ * NW;  // queries per workgroup
   static constexpr int NT = 64 * NW;
-  static constexpr int KROWB = (D + 4) * 4;  // padded K row: 8 lanes reading 8 rows hit 8 bank groups
-  static constexpr int KTILEB = KT * KROWB;
+  static constexpr int NSL = 5;           // int8 slices per fp32 value
+  static constexpr int KSROW = D + 16;    // bytes per key row of one slice plane (padded: 16 rows, 16 bank groups)
+  static constexpr int KSPLANEB = KT * KSROW;
+  static constexpr int KTILEB = NSL * KSPLANEB + KT * 4;  // the slice planes, then each key's exponent
   static constexpr int VPLANEB = KT * D * 2;  // one bf16 piece of the V tile, [KT/32][4][D][8]
   static constexpr int VTILEB = 3 * VPLANEB;  // the three pieces of the V tile
   static constexpr int CH = D / 4;  // 16-byte chunks per K row
@@ -68,6 +84,7 @@ struct F32Tile {
   static constexpr int LDS_BYTES = 2 * (KTILEB + VTILEB);
   static_assert((KT * CH) % NT == 0, "tile chunks must divide evenly over the threads");
   static_assert(KT % 32 == 0, "key tile is a whole number of 32-key chunks");
+  static_assert(CH == 16 || CH == 32, "a K row spans 16 or 32 lanes (d = 64 or 128)");
   static_assert(VITEMS >= 1 && ((KT / 32) * 4 * D) % NT == 0, "V items must divide evenly over the threads");
 };
 
@@ -100,13 +117,60 @@ __device__ __forceinline__ double add_xor(double x) {
   return a + b;
 }
 
+// Largest value over each row of 16 lanes (DPP: swap neighbours, swap
+// pairs, mirror within 8, mirror within 16).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float max_row16(float x) {
+  x = fmaxf(x, dpp_f32<0xB1>(x));   // quad_perm [1, 0, 3, 2]
+  x = fmaxf(x, dpp_f32<0x4E>(x));   // quad_perm [2, 3, 0, 1]
+  x = fmaxf(x, dpp_f32<0x141>(x));  // row_half_mirror
+  x = fmaxf(x, dpp_f32<0x140>(x));  // row_mirror
+  return x;
+}
+// Largest value over the lane pair (l, l ^ 16) / (l, l ^ 32).
+__device__ __forceinline__ float max_xor16_f32(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Exponent e with |x| < 2^e for the largest magnitude m of a row (0 when the
+// row is all zero, whose slices are then all zero).
+__device__ __forceinline__ int row_exponent(float m) { return __builtin_amdgcn_frexp_expf(m); }
+
+// The five int8 slices of four values of one row whose magnitudes are below
+// 2^e: x = 2^(e-6) sum_a s_a 2^(-7a) + r with |s_a| <= 64 and |r| <= 2^(e-35).
+// Slice a is the remainder rounded to the grid 2^(-7a) (after scaling by
+// 2^(6-e)): adding 1.5 * 2^(23-7a) rounds it to nearest even and leaves the
+// integer s_a in the low byte of the sum's bit pattern; subtracting the
+// rounded value back is exact.  w[a] packs s_a of the four values, value 0 in
+// the low byte.
+__device__ __forceinline__ void slice5(f32x4 x, int e, uint32_t (&w)[5]) {
+  float r[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r[k] = __builtin_amdgcn_ldexpf(x[k], 6 - e);
+#pragma unroll
+  for (int a = 0; a < 5; ++a) {
+    const float M = 12582912.0f / static_cast<float>(1 << (7 * a));  // 1.5 * 2^(23 - 7a), exact
+    uint32_t b[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float f = r[k] + M;
+      b[k] = __float_as_uint(f);
+      if (a < 4) r[k] -= f - M;
+    }
+    w[a] = (b[0] & 0xffu) | ((b[1] & 0xffu) << 8) | ((b[2] & 0xffu) << 16) | (b[3] << 24);
+  }
+}
+
 template <class T>
 __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int N, int n_qt, int total_wg, double c2,
     int q_mode) {
   constexpr int D = T::D, QB = T::QB, KT = T::KT;
-  constexpr int DQ = D / 4;  // contraction columns per lane
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
@@ -122,19 +186,39 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
   float* Oh = O + head;
   const int qrow0 = qt * T::BR + wave * T::WQ;
 
-  // ---- Q fragments: lane (i16, g) holds Q[row][g*D/4 + t], t < D/4.  q_mode
-  // folds the sign of the scale into Q so that c2 > 0 below.
+  // ---- Q slices (B operand of S^T): lane (i16, g) holds, for each 64-column
+  // block h, columns 64h + 16g .. 64h + 16g + 15 of its query row, as five
+  // int8 slices under the row's exponent eq.  q_mode folds the sign of the
+  // scale into Q so that c2 > 0 below.
   const float qmul = static_cast<float>(q_mode);
-  f32x4 qf[QB][DQ / 4];
+  u32x4 qs[QB][D / 64][T::NSL];
+  int eq[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qrow0 + qb * 16 + i16;
+    f32x4 x[D / 64][4];
+    float mx = 0.0f;
 #pragma unroll
-    for (int t4 = 0; t4 < DQ / 4; ++t4) {
-      f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if (row < N) x = *reinterpret_cast<const f32x4*>(Qh + static_cast<size_t>(row) * D + g * DQ + 4 * t4);
-      qf[qb][t4] = x * qmul;
-    }
+    for (int h = 0; h < D / 64; ++h)
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+        if (row < N) v = *reinterpret_cast<const f32x4*>(Qh + static_cast<size_t>(row) * D + 64 * h + 16 * g + 4 * t4);
+        v *= qmul;
+        x[h][t4] = v;
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+      }
+    mx = max_xor32(max_xor16_f32(mx));
+    eq[qb] = row_exponent(mx);
+#pragma unroll
+    for (int h = 0; h < D / 64; ++h)
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        uint32_t w[T::NSL];
+        slice5(x[h][t4], eq[qb], w);
+#pragma unroll
+        for (int a2 = 0; a2 < T::NSL; ++a2) qs[qb][h][a2][t4] = w[a2];
+      }
   }
 
   f32x4 acc[QB][D / 16];
@@ -147,9 +231,9 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
     for (int n = 0; n < D / 16; ++n) acc[qb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // V item it of this thread: 32-key chunk c, key class g8 (keys 4i' + g8 of
-  // the chunk, i' < 8) and column vcol.  Lanes of a wave take consecutive
-  // columns, so each of the 8 loads reads whole rows of V.
+  // V item it of this thread: 32-key chunk c, key class g8 (keys
+  // 16 (i / 4) + 4 g8 + i % 4 of the chunk, i < 8) and column vcol.  Lanes of a
+  // wave take consecutive columns, so each of the 8 loads reads whole rows.
   u32x4 kreg[T::LOADS];
   float vreg[T::VITEMS][8];
   // full: tile j lies wholly below N (no key needs the bounds check).
@@ -171,7 +255,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
       const int c = cg >> 2, g8 = cg & 3;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int key = j * KT + 32 * c + 16 * (i >> 2) + 4 * (i & 3) + g8;
+        const int key = j * KT + 32 * c + 16 * (i >> 2) + 4 * g8 + (i & 3);
         vreg[it][i] = (full || key < N) ? Vh[static_cast<size_t>(key) * D + vcol] : 0.0f;
       }
     }
@@ -179,11 +263,24 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
   auto stage_store = [&](int buf) __attribute__((always_inline)) {
     char* kt = smem + buf * (T::KTILEB + T::VTILEB);
     char* vt = kt + T::KTILEB;
+    // K rows as int8 slices under each row's own exponent.  The CH lanes
+    // holding one row (16 or 32 consecutive lanes) agree on its largest
+    // magnitude first.
 #pragma unroll
     for (int u = 0; u < T::LOADS; ++u) {
       const int idx = tid + u * T::NT;
       const int row = idx / T::CH, ch = idx % T::CH;
-      lds_store16(kt, row * T::KROWB + ch * 16, kreg[u]);
+      const f32x4 x = __builtin_bit_cast(f32x4, kreg[u]);
+      float mx = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+      mx = max_row16(mx);
+      if constexpr (T::CH == 32) mx = max_xor16_f32(mx);
+      const int e = row_exponent(mx);
+      uint32_t w[T::NSL];
+      slice5(x, e, w);
+#pragma unroll
+      for (int a2 = 0; a2 < T::NSL; ++a2)
+        *reinterpret_cast<uint32_t*>(kt + a2 * T::KSPLANEB + row * T::KSROW + 4 * ch) = w[a2];
+      if (ch == 0) *reinterpret_cast<int*>(kt + T::NSL * T::KSPLANEB + 4 * row) = e;
     }
     // Split each V value into three bf16 pieces by truncation: x1 keeps the
     // top 16 bits of x, x2 the top 16 bits of x - x1, x3 = x - x1 - x2 (both
@@ -238,25 +335,43 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
     const char* kt = smem + buf * (T::KTILEB + T::VTILEB);
     const char* vt = kt + T::KTILEB;
 
-    // ---- S^T = K Q^T in fp64
+    // ---- S^T = K Q^T from the int8 slices: for each 16-key block, the slice
+    // products with a + b = t accumulate exactly in acc_t (|acc_t| < 2^21),
+    // then s = 2^(eq + ek - 12) sum_t acc_t 2^(-7t) in fp64, combined as
+    // 2^-35 (acc01 2^28 + acc23 2^14 + acc45) with acc01 = 2^7 acc_0 + acc_1
+    // etc. formed exactly in int32.
     f64x4 s[QB][KT / 16];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < KT / 16; ++kb) s[qb][kb] = f64x4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll
     for (int kb = 0; kb < KT / 16; ++kb) {
+      i32x4 ks[D / 64][T::NSL];
 #pragma unroll
-      for (int t4 = 0; t4 < DQ / 4; ++t4) {
-        const f32x4 kf = __builtin_bit_cast(
-            f32x4, lds_load16(kt, (kb * 16 + i16) * T::KROWB + (g * DQ + 4 * t4) * 4));
+      for (int h = 0; h < D / 64; ++h)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const double a = static_cast<double>(kf[e]);
+        for (int a2 = 0; a2 < T::NSL; ++a2)
+          ks[h][a2] = __builtin_bit_cast(i32x4, lds_load16(kt, a2 * T::KSPLANEB + (kb * 16 + i16) * T::KSROW + 64 * h + 16 * g));
+      const i32x4 ek = __builtin_bit_cast(i32x4, lds_load16(kt, T::NSL * T::KSPLANEB + (kb * 16 + 4 * g) * 4));
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            s[qb][kb] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, static_cast<double>(qf[qb][t4][e]),
-                                                             s[qb][kb], 0, 0, 0);
+      for (int qb = 0; qb < QB; ++qb) {
+        i32x4 at[2 * T::NSL - 4];
+#pragma unroll
+        for (int t = 0; t < 2 * T::NSL - 4; ++t) at[t] = i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int h = 0; h < D / 64; ++h)
+#pragma unroll
+          for (int a2 = 0; a2 < T::NSL; ++a2)
+#pragma unroll
+            for (int b2 = 0; b2 < T::NSL; ++b2)
+              if (a2 + b2 <= 5)
+                at[a2 + b2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ks[h][a2], __builtin_bit_cast(i32x4, qs[qb][h][b2]),
+                                                                    at[a2 + b2], 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int a01 = at[0][r] * 128 + at[1][r];
+          const int a23 = at[2][r] * 128 + at[3][r];
+          const int a45 = at[4][r] * 128 + at[5][r];
+          const double x = fma(static_cast<double>(a01), 268435456.0,
+                               fma(static_cast<double>(a23), 16384.0, static_cast<double>(a45)));
+          s[qb][kb][r] = __builtin_amdgcn_ldexp(x, eq[qb] + ek[r] - 47);
         }
       }
     }
@@ -268,7 +383,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
       for (int kb = 0; kb < KT / 16; ++kb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int key = key0 + kb * 16 + 4 * r + g;
+          const int key = key0 + kb * 16 + 4 * g + r;
           if (key >= N)
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) s[qb][kb][r] = -INFINITY;
