@@ -135,6 +135,50 @@ def test_peaked_rows(dtype):
     check_case(f"peaked {dtype}", q, k, v, 0.125, dtype)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("spread", [0, 10, 24])
+def test_f32_wide_range_rows(d, spread):
+    # fp32 scores are formed from int8 slices of each row under a power of two
+    # 2^e above the row's largest magnitude; the slices hold every bit within
+    # 2^-35 of 2^e, so the score error is bounded by the row maxima rather than
+    # by the products themselves:
+    #     |ds_ij| <= |scale| * d * 2^-32 * max_c |q_ic| * max_c |k_jc|.
+    # Entries here are log-uniform over 2^-spread .. 2^spread (random signs),
+    # rows scaled by 2^-8 .. 2^8 as well, so small entries of q meet large
+    # entries of k.  The check: the usual fp32 bound plus what the score
+    # bound allows (LSE moves by at most max_j |ds_ij|; O by at most twice
+    # that times max |v|).
+    B, H, N = 1, 2, 300
+    g = torch.Generator("cpu").manual_seed(4000 + 10 * d + spread)
+
+    def wide(n):
+        mag = torch.exp2((torch.rand(B, H, n, d, generator=g) * 2 - 1) * spread)
+        sign = torch.where(torch.rand(B, H, n, d, generator=g) < 0.5, -1.0, 1.0)
+        rows = torch.exp2(torch.randint(-8, 9, (B, H, n, 1), generator=g).float())
+        return (mag * sign * rows / 2.0 ** (spread / 2)).float().contiguous()
+
+    q, k = wide(N), wide(N)
+    v = torch.randn(B, H, N, d, generator=g)
+    scale = 1.0 / math.sqrt(d)
+    # keep scores finite and moderate: normalise so the largest |s| is ~ 60
+    qk = (q.double() @ k.double().transpose(-1, -2)).abs().amax()
+    q = (q * float(60.0 / (float(qk) * scale))).float().contiguous()
+    go, gl = run_gpu(q, k, v, scale)
+    ro, rl = run_oracle(q, k, v, scale)
+    qmax = q.double().abs().amax(-1).numpy()                  # [B, H, N]
+    kmax = k.double().abs().amax(-1).amax(-1).numpy()[..., None]  # [B, H, 1]
+    ds = float(np.float32(scale)) * d * 2.0 ** -32 * qmax * kmax  # per query row
+    vmax = float(v.abs().max())
+    err_o = np.abs(go - ro).max(-1)
+    err_l = np.abs(gl - rl)
+    tol_l = f32_tolerance(rl) + ds
+    tol_o = F32_ATOL + 2 * ds * vmax
+    _log(f"[parity] f32 wide range d={d} spread=2^{spread}: max|dO|={err_o.max():.3e} max|dLSE|={err_l.max():.3e} "
+         f"max score bound={ds.max():.3e}")
+    assert np.all(err_l <= tol_l), f"LSE off by {err_l.max():.3e}"
+    assert np.all(err_o <= tol_o), f"O off by {err_o.max():.3e}"
+
+
 @pytest.mark.parametrize("B,H,N", [(1, 256, 200), (2, 64, 300), (1, 255, 256), (1, 4, 777), (1, 8, 4000),
                                    (1, 16, 1000), (1, 1, 65)])
 def test_f32_d64_all_tilings(B, H, N):
