@@ -62,6 +62,10 @@
 
 namespace hfa {
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 template <int D_, int QB_, int NW_, int KT_>
 struct F32Tile {
   static constexpr int D = D_;        // head dim (64 or 128)

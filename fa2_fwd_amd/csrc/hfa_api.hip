@@ -41,7 +41,7 @@ using namespace hfa::api;
 #define HFA_F32_D64_TINY_TILE 1, 4, 64
 #endif
 #ifndef HFA_F32_D128_TILE
-#define HFA_F32_D128_TILE 2, 4, 32
+#define HFA_F32_D128_TILE 1, 8, 32
 #endif
 using Bf16D128 = Bf16Tile<128, HFA_BF16_D128_TILE>;
 using Bf16D64 = Bf16Tile<64, HFA_BF16_D64_TILE>;
