@@ -16,9 +16,14 @@
  * O(N) memory, no N x N matrix materialised.  The log-sum-exp output is not on
  * the pages; it is the running max plus the log of the running denominator.
  *
- * Precision.  HFA_F32: fp32 in and out; Q K^T is formed in fp64 on the matrix
- * cores from the exactly widened fp32 inputs, exp2 and P V run in fp32, the
- * log-sum-exp is combined in fp64.  HFA_BF16: bf16 in and out, matrix
+ * Precision.  HFA_F32: fp32 in and out.  Q K^T is formed from exact int8
+ * slices of each row of Q and K (five slices under a power of two above the
+ * row's largest magnitude) on the int8 matrix cores, accumulated exactly and
+ * combined in fp64: the score error is at most |scale| d 2^-32 max|q| max|k|.
+ * P V runs on the bf16 matrix cores from exact three-piece bf16 splits of P
+ * and V (six of the nine piece products; each dropped one is below 2^-21 of
+ * its |p v| term) with fp32 accumulation; exp2 runs in fp32 and the
+ * denominator and log-sum-exp are combined in fp64.  HFA_BF16: bf16 in and out, matrix
  * products on bf16 matrix cores with fp32 accumulation, softmax in fp32,
  * P rounded to bf16 (round-to-nearest-even) for P V, O rounded to bf16 once.
  *
