@@ -36,6 +36,13 @@ if ROOT not in sys.path:
 # MI355X published dense matrix-core peaks (TFLOP/s) and HBM bandwidth (GB/s).
 MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "f64": 78.6}
 HBM_PEAK_GBS = 8000.0
+# What each attention path computes in (the data type alone does not say it).
+ARITH = {
+    "bf16": "bf16 matrix products with fp32 accumulation, fp32 softmax",
+    "f32": "int8 matrix products of exact int8 slices of the fp32 Q and K rows (int32 accumulation, "
+           "fp64 combination); bf16 matrix products of exact three-piece bf16 splits of P and V "
+           "(fp32 accumulation); fp64 running max and denominator, fp32 exp2",
+}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_BYTES = 512 * 1024 * 1024  # calibration copy for the HBM byte counters
 
@@ -157,7 +164,14 @@ def graph_time(w, count: int, reps: int):
         return a.elapsed_time(b) / (reps * count)
 
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+HBM_PEAK_GBS = 8000.0
+# What each attention path computes in (the data type alone does not say it).
+ARITH = {
+    "bf16": "bf16 matrix products with fp32 accumulation, fp32 softmax",
+    "f32": "int8 matrix products of exact int8 slices of the fp32 Q and K rows (int32 accumulation, "
+           "fp64 combination); bf16 matrix products of exact three-piece bf16 splits of P and V "
+           "(fp32 accumulation); fp64 running max and denominator, fp32 exp2",
+}  # MI355X HBM3E
 
 
 def softmax_key(sw) -> str:
@@ -584,6 +598,7 @@ def main() -> int:
             "unit": "TFLOP/s",
             "ms_per_step": round(r2["ms"], 5),
             "dtype": w2.dtype,
+            "arith": ARITH[w2.dtype],
             "config": {"workload": w2.describe(), "B": w2.B, "H": w2.H, "N": w2.N, "d": w2.d},
             "roofline": r2["roofline"],
         }
@@ -640,6 +655,7 @@ def main() -> int:
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
+        "arith": ARITH[w.dtype],
         "data": "synthetic (seeded N(0,1))",
         "config": {"workload": w.describe(), "B": w.B, "H": w.H, "N": w.N, "d": w.d, "seed": w.seed},
         "roofline": main_res["roofline"],
