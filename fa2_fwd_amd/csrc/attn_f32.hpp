@@ -169,6 +169,10 @@ __device__ __forceinline__ void slice5(f32x4 x, int e, uint32_t (&w)[5]) {
   }
 }
 
+#ifndef HFA_F32_SKEW
+#define HFA_F32_SKEW 1
+#endif
+
 template <class T>
 __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
@@ -180,6 +184,13 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int i16 = lane & 15, g = lane >> 4;
+  // With 8 waves, waves 4..7 (one per SIMD) take the tile's phases in another
+  // order: they store their half of the next tile at the start of the
+  // interval instead of at its end (and request the one after it straight
+  // away), so their staging work overlaps the other wave's score products and
+  // the other wave's staging overlaps their P V products.
+  constexpr bool kSkew = HFA_F32_SKEW && T::NW == 8;
+  const bool late = kSkew && __builtin_amdgcn_readfirstlane(tid >> 6) >= T::NW / 2;
 
   const int tile = xcd_remap(blockIdx.x, total_wg);
   const int bh = tile / n_qt, qt = tile - bh * n_qt;
@@ -318,6 +329,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
   const int ntiles = (N + KT - 1) / KT;
   stage_load(0, std::false_type{});
   stage_store(0);
+  if (late && ntiles > 1) stage_load(1, std::false_type{});
   __syncthreads();
 
   // One key tile.  buf is the LDS buffer of tile j (j & 1), a compile-time
@@ -332,10 +344,27 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
       else
         return static_cast<int>(decltype(buf_tag)::value);
     }();
-    if (steady)
-      stage_load(j + 1, std::true_type{});
-    else if (j + 1 < ntiles)
-      stage_load(j + 1, std::false_type{});
+    if constexpr (kSkew) {
+      if (late) {
+        // the late waves' half of tile j + 1, requested at the start of tile
+        // j - 1, then their request for tile j + 2
+        if (steady || j + 1 < ntiles) stage_store(buf ^ 1);
+        if (steady)
+          stage_load(j + 2, std::true_type{});
+        else if (j + 2 < ntiles)
+          stage_load(j + 2, std::false_type{});
+      } else {
+        if (steady)
+          stage_load(j + 1, std::true_type{});
+        else if (j + 1 < ntiles)
+          stage_load(j + 1, std::false_type{});
+      }
+    } else {
+      if (steady)
+        stage_load(j + 1, std::true_type{});
+      else if (j + 1 < ntiles)
+        stage_load(j + 1, std::false_type{});
+    }
     const char* kt = smem + buf * (T::KTILEB + T::VTILEB);
     const char* vt = kt + T::KTILEB;
 
@@ -465,11 +494,21 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
       }
     }
 
-    if (steady || j + 1 < ntiles) stage_store(buf ^ 1);
-    __syncthreads();
+    if constexpr (kSkew) {
+      if (!late && (steady || j + 1 < ntiles)) stage_store(buf ^ 1);
+      // LDS traffic only: the late waves' requests for tile j + 2 stay in flight
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      if (steady || j + 1 < ntiles) stage_store(buf ^ 1);
+      __syncthreads();
+    }
   };
   int j = 0;
-  for (; j + 3 < ntiles; j += 2) {
+  // A trip of two steady tiles requests tiles up to j + 2 (j + 3 for the late
+  // waves of the skewed order) and needs them whole.
+  for (; j + (kSkew ? 4 : 3) < ntiles; j += 2) {
     tile_step(j, std::integral_constant<int, 0>{}, std::true_type{});
     tile_step(j + 1, std::integral_constant<int, 1>{}, std::true_type{});
   }
