@@ -96,6 +96,26 @@ def load_traffic(w):
     return entry
 
 
+# Seconds of untimed launches after the W warm-up steps, so that the shader
+# clock has ramped before timing: a short kernel (0.27 ms at N=2048 fp32) times
+# ~20 % slower after 10 launches than after 0.5 s of them.
+CLOCK_RAMP_S = 0.5
+
+
+def warm_up(launch, warmup: int, ramp_s: float) -> None:
+    """W launches, then more of the same until ramp_s seconds have passed."""
+    import torch
+
+    for _ in range(warmup):
+        launch()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < ramp_s:
+        for _ in range(8):
+            launch()
+        torch.cuda.synchronize()
+
+
 def time_gpu(w, steps: int, warmup: int):
     import torch
 
@@ -108,9 +128,7 @@ def time_gpu(w, steps: int, warmup: int):
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    for _ in range(warmup):
-        hfa.attn_fwd(q, k, v, w.scale, out=o, lse=lse, stream=stream)
-    torch.cuda.synchronize()
+    warm_up(lambda: hfa.attn_fwd(q, k, v, w.scale, out=o, lse=lse, stream=stream), warmup, CLOCK_RAMP_S)
     # One event before each launch and one after the last, all on the launch
     # stream: their span is the timed region, their gaps the per-launch times.
     events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
@@ -164,14 +182,6 @@ def graph_time(w, count: int, reps: int):
         return a.elapsed_time(b) / (reps * count)
 
 
-HBM_PEAK_GBS = 8000.0
-# What each attention path computes in (the data type alone does not say it).
-ARITH = {
-    "bf16": "bf16 matrix products with fp32 accumulation, fp32 softmax",
-    "f32": "int8 matrix products of exact int8 slices of the fp32 Q and K rows (int32 accumulation, "
-           "fp64 combination); bf16 matrix products of exact three-piece bf16 splits of P and V "
-           "(fp32 accumulation); fp64 running max and denominator, fp32 exp2",
-}  # MI355X HBM3E
 
 
 def softmax_key(sw) -> str:
@@ -260,9 +270,7 @@ def time_hbm_op(op: str, wl, steps: int, warmup: int):
 
     launch = HBM_OPS[op]["launcher"](wl)
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        launch(stream)
-    torch.cuda.synchronize()
+    warm_up(lambda: launch(stream), warmup, CLOCK_RAMP_S)
     events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     for i in range(steps):
         events[i].record(stream)
@@ -648,6 +656,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warm_s": CLOCK_RAMP_S,
         "ms_per_step": round(main_res["ms"], 5),
         "ms_median": round(main_res["ms_median"], 5),
         "ms_min": round(main_res["ms_min"], 5),
