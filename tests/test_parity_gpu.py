@@ -179,6 +179,20 @@ def test_f32_wide_range_rows(d, spread):
     assert np.all(err_o <= tol_o), f"O off by {err_o.max():.3e}"
 
 
+@pytest.mark.parametrize("N", [1, 64, 65, 128, 129, 192, 257, 320, 333, 449])
+def test_f32_d64_few_key_tiles(N):
+    # 256 heads put every N here on the 256-row tiling (one workgroup per CU at
+    # least), with 1 to 8 key tiles of 64: the waves that stage the next tile
+    # early request one tile further ahead, so the first tiles, the ragged
+    # last one and the switch from steady two-tile trips to single steps are
+    # all exercised.
+    B, H = 1, 256
+    assert hfa.hfa_block_rows(hfa.HFA_F32, B, H, N, 64) == 256
+    q, k, v = W.make_inputs(B, H, N, 64, "f32", seed=5000 + N, qk_mult=2.0)
+    rows = W.sample_rows(N, 6, seed=N + 1)
+    check_case(f"f32 d=64 B=1 H=256 N={N} (few key tiles)", q, k, v, 0.125, "f32", rows=rows)
+
+
 @pytest.mark.parametrize("B,H,N", [(1, 256, 200), (2, 64, 300), (1, 255, 256), (1, 4, 777), (1, 8, 4000),
                                    (1, 16, 1000), (1, 1, 65)])
 def test_f32_d64_all_tilings(B, H, N):
