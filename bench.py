@@ -36,6 +36,12 @@ if ROOT not in sys.path:
 # MI355X published dense matrix-core peaks (TFLOP/s) and HBM bandwidth (GB/s).
 MFMA_PEAK_TFLOPS = {"bf16": 2516.6, "f32": 157.3, "f64": 78.6}
 HBM_PEAK_GBS = 8000.0
+# The fp32 path's products run on the int8 and bf16 matrix cores from exact
+# splits of the fp32 values.  Per 16 queries x 16 keys x 64 columns (65536
+# counted flop) it issues 19 v_mfma_i32_16x16x64_i8 and 12
+# v_mfma_f32_16x16x32_bf16, 16 cycles each: 132 counted flop per cycle per
+# SIMD, 324.7 TFLOP/s over 1024 SIMDs at 2.4 GHz (the same at d = 128).
+F32_ENGINE_PEAK_TFLOPS = 65536 / ((19 + 12) * 16) * 1024 * 2.4e9 / 1e12
 # What each attention path computes in (the data type alone does not say it).
 ARITH = {
     "bf16": "bf16 matrix products with fp32 accumulation, fp32 softmax",
@@ -156,6 +162,10 @@ def time_gpu(w, steps: int, warmup: int):
         "algorithmic_bytes": algorithmic_bytes(w),
         "kernel": kernel_key(w),
     }
+    if w.dtype == "f32":
+        # beside the fp32 peak, the ceiling of the matrix-core instructions issued
+        roofline["engine_peak"] = round(F32_ENGINE_PEAK_TFLOPS, 1)
+        roofline["engine_frac"] = round(tflops / F32_ENGINE_PEAK_TFLOPS, 4)
     return {"ms": ms, "tflops": tflops, "wall_s": wall, "roofline": roofline,
             "ms_median": per_launch[len(per_launch) // 2], "ms_min": per_launch[0]}
 
