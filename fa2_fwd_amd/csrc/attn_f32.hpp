@@ -334,8 +334,12 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
 
   // One key tile.  buf is the LDS buffer of tile j (j & 1), a compile-time
   // constant in the unrolled loop below so that the buffer offset folds into
-  // the LDS instructions; steady: tile j + 1 is wholly below N and tile j is
-  // not the last, so no bounds check, no masking and no end-of-loop test.
+  // the LDS instructions; steady: every tile requested in this step (j + 1,
+  // or j + 2 for the late waves) is wholly below N and tile j is not the
+  // last, so no bounds check, no masking and no end-of-loop test.  The next
+  // tile goes into the other buffer, which no wave reads during this tile:
+  // the early waves request it at the start and store it at the end, the
+  // late waves store it at the start (requested one tile earlier).
   auto tile_step = [&](int j, auto buf_tag, auto steady_tag) __attribute__((always_inline)) {
     constexpr bool steady = decltype(steady_tag)::value;
     const int buf = [&] {
