@@ -281,9 +281,14 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
     // K rows as int8 slices under each row's own exponent.  The CH lanes
     // holding one row (16 or 32 consecutive lanes) agree on its largest
     // magnitude first.
+    // The thread index goes through an empty asm statement so that the LDS
+    // addresses below are recomputed here (a few shifts) rather than hoisted
+    // out of the key loop and spilled.
+    int tid_here = tid;
+    asm volatile("" : "+v"(tid_here));
 #pragma unroll
     for (int u = 0; u < T::LOADS; ++u) {
-      const int idx = tid + u * T::NT;
+      const int idx = tid_here + u * T::NT;
       const int row = idx / T::CH, ch = idx % T::CH;
       const f32x4 x = __builtin_bit_cast(f32x4, kreg[u]);
       float mx = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
