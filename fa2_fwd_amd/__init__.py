@@ -12,10 +12,12 @@ from __future__ import annotations
 
 import ctypes
 import math
+import os
 from pathlib import Path
 
 _PKG = Path(__file__).resolve().parent
-LIB_PATH = _PKG / "libhfa.so"
+# HFA_LIB selects another build of the library (e.g. one with host sanitizers).
+LIB_PATH = Path(os.environ["HFA_LIB"]) if os.environ.get("HFA_LIB") else _PKG / "libhfa.so"
 
 HFA_F32 = 0
 HFA_BF16 = 1

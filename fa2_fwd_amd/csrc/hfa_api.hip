@@ -203,6 +203,7 @@ const char* hfa_status_str(hfa_status s) {
     case HFA_ERR_NO_DEVICE: return "no current gfx950 HIP device";
     case HFA_ERR_LAUNCH: return "kernel launch failed";
     case HFA_ERR_EPS: return "eps must be finite and > 0";
+    default: break;
   }
   return "unknown status";
 }

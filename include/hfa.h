@@ -48,9 +48,15 @@
 extern "C" {
 #endif
 
+/* In both enums the two *_RANGE_ entries are not values to pass: they make
+ * every 32-bit int a valid value of the type, so that an unknown code passed
+ * from C (or any foreign-function caller) is rejected with a status instead
+ * of being undefined behaviour in the C++ implementation. */
 typedef enum {
   HFA_F32 = 0,  /* fp32 (4-byte IEEE binary32) elements */
-  HFA_BF16 = 1  /* bf16 (2-byte, upper half of binary32) elements */
+  HFA_BF16 = 1, /* bf16 (2-byte, upper half of binary32) elements */
+  HFA_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  HFA_DTYPE_RANGE_MAX_ = 2147483647
 } hfa_dtype;
 
 typedef enum {
@@ -63,7 +69,9 @@ typedef enum {
   HFA_ERR_ALIAS = 6,       /* o or lse overlaps q, k, v or each other */
   HFA_ERR_NO_DEVICE = 7,   /* no HIP device is current, or it is not gfx950 */
   HFA_ERR_LAUNCH = 8,      /* the kernel launch itself failed */
-  HFA_ERR_EPS = 9          /* hfa_rmsnorm: eps is not a finite value > 0 */
+  HFA_ERR_EPS = 9,         /* hfa_rmsnorm: eps is not a finite value > 0 */
+  HFA_STATUS_RANGE_MIN_ = -2147483647 - 1,
+  HFA_STATUS_RANGE_MAX_ = 2147483647
 } hfa_status;
 
 /* Attention forward.

@@ -40,7 +40,8 @@ from pathlib import Path
 import numpy as np
 
 _HERE = Path(__file__).resolve().parent
-LIB_PATH = _HERE / "libhfa_ref.so"
+# HFA_REF_LIB selects another build (e.g. one with the sanitizers).
+LIB_PATH = Path(os.environ["HFA_REF_LIB"]) if os.environ.get("HFA_REF_LIB") else _HERE / "libhfa_ref.so"
 
 
 def default_threads() -> int:
