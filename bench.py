@@ -122,7 +122,7 @@ def warm_up(launch, warmup: int, ramp_s: float) -> None:
         torch.cuda.synchronize()
 
 
-def time_gpu(w, steps: int, warmup: int):
+def time_gpu(w, steps: int, warmup: int, ramp_s: float = CLOCK_RAMP_S):
     import torch
 
     import fa2_fwd_amd as hfa
@@ -134,7 +134,7 @@ def time_gpu(w, steps: int, warmup: int):
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    warm_up(lambda: hfa.attn_fwd(q, k, v, w.scale, out=o, lse=lse, stream=stream), warmup, CLOCK_RAMP_S)
+    warm_up(lambda: hfa.attn_fwd(q, k, v, w.scale, out=o, lse=lse, stream=stream), warmup, ramp_s)
     # One event before each launch and one after the last, all on the launch
     # stream: their span is the timed region, their gaps the per-launch times.
     events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
@@ -163,9 +163,15 @@ def time_gpu(w, steps: int, warmup: int):
         "kernel": kernel_key(w),
     }
     if w.dtype == "f32":
-        # beside the fp32 peak, the ceiling of the matrix-core instructions issued
-        roofline["engine_peak"] = round(F32_ENGINE_PEAK_TFLOPS, 1)
-        roofline["engine_frac"] = round(tflops / F32_ENGINE_PEAK_TFLOPS, 4)
+        # The fp32 path issues int8 and bf16 matrix-core instructions, not fp32 ones: its
+        # roofline is the ceiling of those instructions; the fp32 MFMA peak stays as context
+        # (what fp32 matrix cores would allow for the same counted work).
+        roofline["peak"] = round(F32_ENGINE_PEAK_TFLOPS, 1)
+        roofline["frac"] = round(tflops / F32_ENGINE_PEAK_TFLOPS, 4)
+        roofline["peak_basis"] = ("ceiling of the instructions issued: 19 v_mfma_i32_16x16x64_i8 + 12 "
+                                  "v_mfma_f32_16x16x32_bf16 (16 cycles each) per 65536 counted flop")
+        roofline["fp32_peak"] = peak
+        roofline["fp32_frac"] = round(tflops / peak, 4)
     return {"ms": ms, "tflops": tflops, "wall_s": wall, "roofline": roofline,
             "ms_median": per_launch[len(per_launch) // 2], "ms_min": per_launch[0]}
 
@@ -454,6 +460,66 @@ def cpu_baseline(w, target_s: float):
     }
 
 
+def host_info() -> dict:
+    """The host the oracle timings ran on: CPU model, logical CPUs, CPUs this process may use."""
+    import oracle
+
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count()
+    return {"cpu_model": model, "nproc": os.cpu_count(), "cpus_usable": usable,
+            "oracle_threads": oracle.default_threads()}
+
+
+def oracle_time(w, threads: int):
+    """Seconds the oracle (fp64 definition, score rows materialised) takes for the whole workload."""
+    import oracle
+    from fa2_fwd_amd import workloads as W
+
+    qa, ka, va = (W.to_oracle_array(t) for t in W.workload_inputs(w))
+    t0 = time.perf_counter()
+    oracle.attn_fwd(qa, ka, va, w.scale, threads=threads)
+    return time.perf_counter() - t0
+
+
+def oracle_times(configs, main_cfg: int, cpu_main, single_thread=(1, 2, 3)):
+    """Oracle seconds per workload: whole workloads on all oracle threads, the small ones
+    (`single_thread`) also on one thread; the main workload (too large for the oracle in full)
+    by extrapolation from its sampled cpu_baseline."""
+    import oracle
+
+    threads = oracle.default_threads()
+    out = {}
+    for n, wn in sorted(configs.items()):
+        if n == main_cfg and wn.flops > 1e12:
+            if cpu_main is not None:
+                out[n] = {"rows": "sampled (cpu_baseline)", "threads": cpu_main["cores"],
+                          "s_extrapolated": round(wn.flops / (cpu_main["value"] * 1e12), 1),
+                          "gflops": round(cpu_main["value"] * 1e3, 2)}
+            continue
+        if wn.flops > 1e12:
+            continue
+        t = oracle_time(wn, threads)
+        entry = {"rows": "all", "threads": threads, "s": round(t, 3), "gflops": round(wn.flops / t / 1e9, 2)}
+        if n in single_thread:
+            t1 = oracle_time(wn, 1)
+            entry.update({"s_1thread": round(t1, 3), "gflops_1thread": round(wn.flops / t1 / 1e9, 2)})
+        log(f"[bench] oracle {wn.describe()}: {t:.2f} s on {threads} threads"
+            + (f", {entry['s_1thread']:.2f} s on 1" if "s_1thread" in entry else ""))
+        out[n] = entry
+    return out
+
+
 def profile_pass_hbm_op(op: str, wl, launches: int) -> None:
     """A few launches of an HBM-bound operation and one device copy of COPY_BYTES, for counter runs."""
     import torch
@@ -470,8 +536,10 @@ def profile_pass_hbm_op(op: str, wl, launches: int) -> None:
     log(f"[profile] {launches} launches of {wl.describe()} and one {COPY_BYTES} B copy done")
 
 
-def profile_pass(w, launches: int) -> None:
-    """A few kernel launches and one device copy of COPY_BYTES, for counter runs."""
+def profile_pass(w, launches: int, warmup: int, ramp_s: float) -> None:
+    """For counter runs: the timed path's warm-up (W launches, then ramp_s seconds of them),
+    `launches` more launches, and one device copy of COPY_BYTES.  The summaries use the last
+    `launches` dispatches of the kernel, taken at the clock the timed launches run at."""
     import torch
 
     import fa2_fwd_amd as hfa
@@ -479,8 +547,12 @@ def profile_pass(w, launches: int) -> None:
 
     dev = torch.device("cuda:0")
     q, k, v = (t.to(dev) for t in W.workload_inputs(w))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    warm_up(lambda: hfa.attn_fwd(q, k, v, w.scale, out=o, lse=lse, stream=stream), warmup, ramp_s)
     for _ in range(launches):
-        hfa.attn_fwd(q, k, v, w.scale)
+        hfa.attn_fwd(q, k, v, w.scale, out=o, lse=lse, stream=stream)
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
@@ -499,19 +571,23 @@ def _read_counter(dirpath: str, counter: str):
         with open(path) as f:
             for row in csv.DictReader(f):
                 if row.get("Counter_Name") == counter:
-                    out.append((row.get("Kernel_Name", ""), float(row["Counter_Value"])))
-    return out
+                    out.append((int(row.get("Dispatch_Id", 0)), row.get("Kernel_Name", ""),
+                                float(row["Counter_Value"])))
+    out.sort()
+    return [(name, v) for _, name, v in out]
 
 
-def summarize_pmc(w, fetch_dir: str, write_dir: str, op: str = "attn") -> None:
+def summarize_pmc(w, fetch_dir: str, write_dir: str, op: str = "attn", last: int = 0) -> None:
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the measured kernel (attention, or the
     HBM-bound operation `op`), each scaled by what the same counter reads for the copy of
-    known size."""
+    known size; over the last `last` dispatches of the kernel (all when 0)."""
     marker = "attn_fwd" if op == "attn" else HBM_OPS[op]["marker"]
     result = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         rows = _read_counter(d, counter)
         kern = [v for name, v in rows if marker in name]
+        if last > 0:
+            kern = kern[-last:]
         # The device-to-device copy is HIP's blit kernel; fall back to the
         # largest other dispatch if the runtime names it differently.
         copies = [v for name, v in rows if "copyBuffer" in name]
@@ -546,6 +622,171 @@ def summarize_pmc(w, fetch_dir: str, write_dir: str, op: str = "attn") -> None:
     log(f"[pmc] {w.describe()}: HBM {total / 1e6:.1f} MB/launch vs algorithmic {alg / 1e6:.1f} MB")
 
 
+def _csv_rows(dirpath: str, suffix: str):
+    files = glob.glob(os.path.join(dirpath, "**", f"*{suffix}"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {dirpath}")
+    rows = []
+    for path in files:
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _last_json_line(path: str):
+    with open(path) as f:
+        lines = [ln for ln in f if ln.strip().startswith("{")]
+    return json.loads(lines[-1])
+
+
+def _config_ms(line: dict, n: int):
+    """ms_per_step of workload n in a bench JSON line (headline, secondary or all_configs)."""
+    for e in line.get("all_configs") or []:
+        if e["config"] == n:
+            return e["ms_per_step"]
+    if line.get("config", {}).get("workload") == W_describe(n):
+        return line["ms_per_step"]
+    sec = line.get("secondary")
+    if sec and sec["config"]["workload"] == W_describe(n):
+        return sec["ms_per_step"]
+    return None
+
+
+def W_describe(n: int) -> str:
+    from fa2_fwd_amd import workloads as W
+
+    return W.CONFIGS[n].describe()
+
+
+def kernel_profile_name(w) -> str:
+    return f"attn_fwd_{w.dtype}_d{w.d}_N{w.N}"
+
+
+def summarize_trace(n: int, trace_dir: str, trace_json: str, bench_json: str | None, command: str) -> None:
+    """profiles/<kernel>.md: kernel durations of a traced run of the timed path, beside the
+    event timing of that run and the unprofiled bench run of the same job."""
+    from fa2_fwd_amd import workloads as W
+
+    w = W.CONFIGS[n]
+    traced = _last_json_line(trace_json)
+    steps = int(traced["steps"])
+    rows = [r for r in _csv_rows(trace_dir, "kernel_trace.csv") if "attn_fwd" in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
+    timed = durs[-steps:]
+    avg_timed = sum(timed) / len(timed)
+    st = [r for r in _csv_rows(trace_dir, "kernel_stats.csv") if "attn_fwd" in r["Name"]][0]
+    traced_ms = float(traced["ms_per_step"])
+    bench_ms = None
+    if bench_json:
+        bench_ms = _config_ms(_last_json_line(bench_json), n)
+    tflops_trace = w.flops / (avg_timed * 1e-9) / 1e12
+    roof = traced["roofline"]
+    frac_trace = tflops_trace / roof["peak"]
+    traffic = load_traffic(w)
+    lines = [f"# {kernel_profile_name(w)} -- {w.describe()}", "",
+             "## Kernel time (rocprofv3 --kernel-trace --stats)", "",
+             f"Command: `{command}`", "",
+             f"The traced process runs the timed path of `bench.py`: {traced['warmup']} warm-up launches, "
+             f"{traced['warm_s']} s more of them (clock ramp), then {steps} timed launches between HIP events. "
+             f"The last {steps} dispatches of the kernel in the trace are those timed launches.", "",
+             "| kernel | calls (all) | avg ns (all) | min ns | max ns |", "|---|---|---|---|---|",
+             f"| `{st['Name'][:100]}` | {st['Calls']} | {float(st['AverageNs']):.0f} | {st['MinNs']} | {st['MaxNs']} |",
+             "", "| figure | ms |", "|---|---|",
+             f"| trace: average duration of the {steps} timed dispatches | {avg_timed / 1e6:.5f} |",
+             f"| the traced run's own event timing (`ms_per_step` of its JSON line) | {traced_ms:.5f} |"]
+    if bench_ms is not None:
+        lines.append(f"| unprofiled `python bench.py` in the same job (`ms_per_step` of this workload) | {bench_ms:.5f} |")
+    lines += ["",
+              f"From the trace: {tflops_trace:.1f} TFLOP/s = {frac_trace:.4f} of the {roof['peak']} TFLOP/s "
+              f"roofline (the line: {roof['achieved']} TFLOP/s, frac {roof['frac']}).",
+              f"Trace average / event ms_per_step of the traced run: {avg_timed / 1e6 / traced_ms:.4f}"
+              + (f"; / unprofiled ms_per_step: {avg_timed / 1e6 / bench_ms:.4f}." if bench_ms else "."), ""]
+    if traffic is not None:
+        t = traffic
+        lines += ["## HBM bytes (rocprofv3 --pmc, one counter per run)", "",
+                  f"Commands: `rocprofv3 --pmc FETCH_SIZE -d gpurun_out/pmc_fetch{n} -o run --output-format csv -- "
+                  f"python bench.py --profile-pass --config {n}` and the same with `WRITE_SIZE` into "
+                  f"`gpurun_out/pmc_write{n}`; then `python bench.py --summarize-pmc gpurun_out/pmc_fetch{n} "
+                  f"gpurun_out/pmc_write{n} --config {n}`.",
+                  f"Each counter is scaled by what it reads for a plain 512 MiB device copy in the same run "
+                  f"(FETCH_SIZE x{t['fetch']['scale']:.4f}, WRITE_SIZE x{t['write']['scale']:.4f}).", "",
+                  "| counter | KiB/dispatch (raw) | copy KiB (raw, 524288 expected) | scaled bytes/launch |",
+                  "|---|---|---|---|",
+                  f"| FETCH_SIZE | {t['fetch']['kernel_kib_per_dispatch']:.1f} | {t['fetch']['copy_kib']:.1f} | "
+                  f"{t['fetch']['bytes_per_launch']:.0f} |",
+                  f"| WRITE_SIZE | {t['write']['kernel_kib_per_dispatch']:.1f} | {t['write']['copy_kib']:.1f} | "
+                  f"{t['write']['bytes_per_launch']:.0f} |", "",
+                  f"HBM traffic per launch: {t['hbm_bytes_per_launch'] / 1e6:.1f} MB; algorithmic (Q, K, V read "
+                  f"once, O and LSE written once): {t['algorithmic_bytes'] / 1e6:.1f} MB.", ""]
+    lines.append(f"Kernel source digest when taken: `{kernel_source_digest()}`.")
+    path = os.path.join(ROOT, "profiles", kernel_profile_name(w) + ".md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log(f"[profile] {path}: trace {avg_timed / 1e6:.5f} ms vs event {traced_ms:.5f} ms"
+        + (f" vs bench {bench_ms:.5f} ms" if bench_ms else ""))
+
+
+SQ_GROUPS = (
+    "GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS "
+    "SQ_WAIT_INST_ANY SQ_WAIT_ANY SQ_WAVE_CYCLES SQ_BUSY_CYCLES",
+    "GRBM_GUI_ACTIVE SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS "
+    "SQ_INSTS_VALU_TRANS_F32 SQ_ACTIVE_INST_ANY SQ_INSTS_SALU",
+)
+
+
+def summarize_sq(n: int, sq1: str, sq2: str, trace_dir: str, launches: int) -> None:
+    """profiles/<kernel>_sq.md from two shader-counter runs and a kernel trace of --profile-pass,
+    each over the last `launches` dispatches (after the timed path's warm-up)."""
+    from fa2_fwd_amd import workloads as W
+
+    w = W.CONFIGS[n]
+    vals: dict[str, list[float]] = {}
+    for d in (sq1, sq2):
+        per: dict[str, dict[int, float]] = {}
+        for r in _csv_rows(d, "counter_collection.csv"):
+            if "attn_fwd" in r["Kernel_Name"]:
+                per.setdefault(r["Counter_Name"], {})[int(r["Dispatch_Id"])] = float(r["Counter_Value"])
+        for name, by_id in per.items():
+            last = [by_id[i] for i in sorted(by_id)[-launches:]]
+            vals.setdefault(name, []).extend(last)
+    c = {k: sum(v) / len(v) for k, v in vals.items()}
+    rows = sorted((r for r in _csv_rows(trace_dir, "kernel_trace.csv") if "attn_fwd" in r["Kernel_Name"]),
+                  key=lambda r: int(r["Dispatch_Id"]))
+    durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows][-launches:]
+    avg_us = sum(durs) / len(durs) / 1e3
+    act = c["GRBM_GUI_ACTIVE"] / 8
+    busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * act)
+    pp = f"python bench.py --profile-pass --config {n} --launches {launches}"
+    lines = [f"# {kernel_profile_name(w)}_sq -- shader counters, {w.describe()}", "",
+             f"Each run: `{pp}` (the timed path's warm-up, then {launches} launches and one 512 MiB copy); "
+             f"figures are averages over the last {launches} dispatches of the kernel.", "",
+             f"- `rocprofv3 --pmc {SQ_GROUPS[0]} -d gpurun_out/sq1_c{n} -o run --output-format csv -- {pp}`",
+             f"- `rocprofv3 --pmc {SQ_GROUPS[1]} -d gpurun_out/sq2_c{n} -o run --output-format csv -- {pp}`",
+             f"- `rocprofv3 --kernel-trace --stats -d gpurun_out/sqtr_c{n} -o run --output-format csv -- {pp}`", "",
+             "| counter (per launch, whole chip) | value |", "|---|---|"]
+    for k in sorted(c):
+        lines.append(f"| {k} | {c[k]:.4g} |")
+    lds = max(c.get("SQ_INSTS_LDS", 0.0), 1.0)
+    lines += ["", f"Kernel time under the trace (last {launches} dispatches): {avg_us:.1f} us.", "", "Derived:", "",
+              f"- GPU-active cycles per XCD: {act:.4g}, i.e. {act / (avg_us * 1e3):.2f} GHz over the traced time "
+              f"(counter and trace runs are separate processes).",
+              f"- Matrix-core busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x active cycles) = {100 * busy:.1f} %.",
+              f"- MFMA instructions: {c['SQ_INSTS_MFMA']:.4g}; LDS instructions: {c['SQ_INSTS_LDS']:.4g}; LDS "
+              f"bank-conflict cycles: {c['SQ_LDS_BANK_CONFLICT']:.4g} ({c['SQ_LDS_BANK_CONFLICT'] / lds:.3f} per LDS "
+              f"instruction).",
+              f"- VALU instructions: {c['SQ_INSTS_VALU']:.4g}, of which transcendental (exp) "
+              f"{c['SQ_INSTS_VALU_TRANS_F32']:.4g}; SALU {c['SQ_INSTS_SALU']:.4g}.",
+              f"- MFMA cycles with VALU issued alongside: "
+              f"{100 * c['SQ_VALU_MFMA_COEXEC_CYCLES'] / max(c['SQ_VALU_MFMA_BUSY_CYCLES'], 1):.1f} % of MFMA busy "
+              f"cycles.", "", f"Kernel source digest when taken: `{kernel_source_digest()}`.", ""]
+    path = os.path.join(ROOT, "profiles", kernel_profile_name(w) + "_sq.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines))
+    log(f"[profile] {path}: {avg_us:.1f} us, MFMA busy {100 * busy:.1f} %, LDS conflicts per LDS instruction "
+        f"{c['SQ_LDS_BANK_CONFLICT'] / lds:.3f}")
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -559,7 +800,20 @@ def main() -> int:
                     help="target oracle time for cpu_baseline (the sizing from short runs lands near 70%% of it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-pass", action="store_true")
-    ap.add_argument("--launches", type=int, default=3)
+    ap.add_argument("--launches", type=int, default=5, help="--profile-pass: launches after the warm-up")
+    ap.add_argument("--ramp-s", type=float, default=CLOCK_RAMP_S,
+                    help="seconds of untimed launches after the W warm-up launches (clock ramp)")
+    ap.add_argument("--no-oracle-times", action="store_true",
+                    help="skip the oracle timings of the small workloads (all_configs[].oracle)")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="write profiles/<kernel>.md from a rocprofv3 --kernel-trace --stats run of this "
+                         "command's timed path (see --trace-json, --bench-json)")
+    ap.add_argument("--trace-json", help="--summarize-trace: the JSON line printed by the traced run")
+    ap.add_argument("--bench-json", help="--summarize-trace: the JSON line of the unprofiled bench run "
+                                         "of the same job")
+    ap.add_argument("--summarize-sq", nargs=3, metavar=("SQ1_DIR", "SQ2_DIR", "TRACE_DIR"),
+                    help="write profiles/<kernel>_sq.md from two shader-counter runs of --profile-pass "
+                         "and a kernel trace of the same pass")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--op", choices=("attn", "softmax", "rmsnorm"), default="attn",
                     help="kernel for --profile-pass / --summarize-pmc / --op-only (--config numbers that "
@@ -583,14 +837,23 @@ def main() -> int:
         return 0
     w = W.CONFIGS[args.config]
     if args.summarize_pmc:
-        summarize_pmc(w, *args.summarize_pmc)
+        summarize_pmc(w, *args.summarize_pmc, last=args.launches)
+        return 0
+    if args.summarize_trace:
+        traced_cmd = (f"rocprofv3 --kernel-trace --stats -d {args.summarize_trace} -o run --output-format csv -- "
+                      f"python bench.py --config {args.config} --steps {args.steps} --warmup {args.warmup} "
+                      f"--secondary 0 --no-all-configs --no-sclk --no-softmax --no-rmsnorm --no-cpu-baseline")
+        summarize_trace(args.config, args.summarize_trace, args.trace_json, args.bench_json, traced_cmd)
+        return 0
+    if args.summarize_sq:
+        summarize_sq(args.config, *args.summarize_sq, args.launches)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this attention forward is a single-GPU kernel; "
               "see the design notes for how it would shard across GPUs.", file=sys.stderr)
         return 2
     if args.profile_pass:
-        profile_pass(w, args.launches)
+        profile_pass(w, args.launches, args.warmup, args.ramp_s)
         return 0
 
     import torch
@@ -605,11 +868,11 @@ def main() -> int:
         print(json.dumps(time_hbm_op(args.op, hbm_configs(args.op)[args.config], args.steps, args.warmup)),
               flush=True)
         return 0
-    main_res = time_gpu(w, args.steps, args.warmup)
+    main_res = time_gpu(w, args.steps, args.warmup, args.ramp_s)
     secondary = None
     if args.secondary and args.secondary != args.config:
         w2 = W.CONFIGS[args.secondary]
-        r2 = time_gpu(w2, args.steps, args.warmup)
+        r2 = time_gpu(w2, args.steps, args.warmup, args.ramp_s)
         secondary = {
             "metric": "attention fwd TFLOP/s",
             "value": round(r2["tflops"], 3),
@@ -619,6 +882,7 @@ def main() -> int:
             "arith": ARITH[w2.dtype],
             "config": {"workload": w2.describe(), "B": w2.B, "H": w2.H, "N": w2.N, "d": w2.d},
             "roofline": r2["roofline"],
+            "cpu_baseline": None,
         }
     all_configs = None
     if not args.no_all_configs:
@@ -629,18 +893,21 @@ def main() -> int:
             elif secondary is not None and n == args.secondary:
                 r = r2
             else:
-                r = time_gpu(W.CONFIGS[n], max(10, args.steps // 2), args.warmup)
+                r = time_gpu(W.CONFIGS[n], max(10, args.steps // 2), args.warmup, args.ramp_s)
             wn = W.CONFIGS[n]
             graph_ms = graph_time(wn, 100, 3) if wn.flops < 1e10 else None
             if graph_ms is not None:
                 log(f"[bench] {wn.describe()}: {graph_ms * 1e3:.2f} us/launch replayed from a graph of 100")
-            all_configs.append({
+            entry = {
                 "config": n, "workload": wn.describe(), "dtype": wn.dtype,
                 "ms_per_step": round(r["ms"], 5), "ms_median": round(r["ms_median"], 5),
                 "ms_min": round(r["ms_min"], 5), "tflops": round(r["tflops"], 3),
-                "frac_of_peak": round(r["tflops"] / MFMA_PEAK_TFLOPS[wn.dtype], 4),
+                "peak": r["roofline"]["peak"], "frac_of_peak": r["roofline"]["frac"],
                 "ms_per_launch_graph": None if graph_ms is None else round(graph_ms, 5),
-            })
+            }
+            if wn.dtype == "f32":
+                entry["fp32_frac"] = r["roofline"]["fp32_frac"]
+            all_configs.append(entry)
     sclk = None if args.no_sclk else observed_sclk(w, 0.5)
     if sclk is not None:
         log(f"[bench] shader clock during {w.describe()}: {sclk:.0f} MHz (median of sysfs samples)")
@@ -658,6 +925,22 @@ def main() -> int:
             entries.append(entry)
         hbm[HBM_OPS[op]["json_key"]] = entries
     cpu = None if args.no_cpu_baseline else cpu_baseline(w, args.cpu_seconds)
+    host = None
+    if not args.no_cpu_baseline:
+        host = host_info()
+        log(f"[bench] host: {host}")
+    if not args.no_cpu_baseline and not args.no_oracle_times:
+        otimes = oracle_times(W.CONFIGS, args.config, cpu)
+        for entry in all_configs or []:
+            entry["oracle"] = otimes.get(entry["config"])
+        if secondary is not None and args.secondary in otimes and "s" in otimes[args.secondary]:
+            o2 = otimes[args.secondary]
+            secondary["cpu_baseline"] = {
+                "value": round(W.CONFIGS[args.secondary].flops / o2["s"] / 1e12, 6), "unit": "TFLOP/s",
+                "cores": o2["threads"], "kind": "oracle",
+                "sample": f"the whole workload (every query row of every head), fp64 definition with the score "
+                          f"rows materialised; {o2['s']:.2f} s",
+            }
     props = torch.cuda.get_device_properties(0)
     line = {
         "metric": "attention fwd TFLOP/s (4*B*H*N^2*d per launch) and fraction of MFMA peak",
@@ -666,7 +949,7 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "warm_s": CLOCK_RAMP_S,
+        "warm_s": args.ramp_s,
         "ms_per_step": round(main_res["ms"], 5),
         "ms_median": round(main_res["ms_median"], 5),
         "ms_min": round(main_res["ms_min"], 5),
@@ -686,6 +969,7 @@ def main() -> int:
         "device_copy_gbs": copy_gbs,
         "observed_sclk_mhz": sclk,
         "device": getattr(props, "gcnArchName", props.name),
+        "host": host,
     }
     print(json.dumps(line), flush=True)
     return 0

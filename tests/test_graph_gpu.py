@@ -13,6 +13,7 @@ import torch
 
 import fa2_fwd_amd as hfa
 from fa2_fwd_amd import workloads as W
+from parity_util import assert_close, run_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -24,10 +25,12 @@ CASES = [("f32", 1, 1, 128, 64), ("f32", 4, 8, 1024, 64), ("bf16", 1, 2, 1000, 1
 def test_graph_replays_match_eager(dtype, B, H, N, d, count):
     print(f"[graph] {dtype} B={B} H={H} N={N} d={d} count={count}", flush=True)
     dev = torch.device("cuda:0")
-    q, k, v = (t.to(dev) for t in W.make_inputs(B, H, N, d, dtype, seed=N + d + count))
+    hq, hk, hv = W.make_inputs(B, H, N, d, dtype, seed=N + d + count)
+    q, k, v = (t.to(dev) for t in (hq, hk, hv))
     scale = 1.0 / math.sqrt(d)
     o_ref, lse_ref = hfa.attn_fwd(q, k, v, scale)
     torch.cuda.synchronize()
+    ref_o, ref_lse = run_oracle(hq, hk, hv, scale)
     other = [t.to(dev) for t in W.make_inputs(B, H, N, d, dtype, seed=7)]
     with hfa.AttnGraph(q, k, v, scale, count=count) as g:
         for rep in range(3):
@@ -37,6 +40,9 @@ def test_graph_replays_match_eager(dtype, B, H, N, d, count):
             torch.cuda.synchronize()
             o, lse = g.launch()
             torch.cuda.synchronize()
+            # each replay against the oracle, then bit for bit against the eager call
+            assert_close(f"graph replay {rep} {dtype} B={B} H={H} N={N} d={d} count={count}",
+                         o.float().cpu().double().numpy(), lse.cpu().double().numpy(), ref_o, ref_lse, dtype)
             assert torch.equal(o, o_ref), f"replay {rep}: O differs from the eager call"
             assert torch.equal(lse, lse_ref), f"replay {rep}: LSE differs from the eager call"
 
