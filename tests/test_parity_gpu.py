@@ -21,7 +21,7 @@ import fa2_fwd_amd as hfa
 import oracle
 from fa2_fwd_amd import workloads as W
 
-from parity_util import (BF16_ATOL, BF16_RTOL, F32_ATOL, assert_close, check_case, f32_tolerance,  # noqa: F401
+from parity_util import (BF16_ATOL, BF16_RTOL, F32_ATOL, _log, assert_close, check_case, f32_tolerance,  # noqa: F401
                          run_gpu, run_oracle)
 
 pytestmark = pytest.mark.gpu
