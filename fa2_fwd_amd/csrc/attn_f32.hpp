@@ -78,14 +78,16 @@ struct F32Tile {
   static constexpr int NSL = 5;           // int8 slices per fp32 value
   static constexpr int KSROW = D + 16;    // bytes per key row of one slice plane (padded: 16 rows, 16 bank groups)
   static constexpr int KSPLANEB = KT * KSROW;
-  static constexpr int KTILEB = NSL * KSPLANEB + KT * 4;  // the slice planes, then each key's exponent
+  static constexpr int KEXPB = NSL * KSPLANEB;  // offset of the per-key exponents (int32)
+  static constexpr int KTILEB = KEXPB + KT * 4;  // the slice planes, then each key's exponent
   static constexpr int VPLANEB = KT * D * 2;  // one bf16 piece of the V tile, [KT/32][4][D][8]
   static constexpr int VTILEB = 3 * VPLANEB;  // the three pieces of the V tile
   static constexpr int CH = D / 4;  // 16-byte chunks per K row
   static constexpr int LOADS = KT * CH / NT;
   // V is staged as (32-key chunk, key class g, column) items of 8 keys each.
   static constexpr int VITEMS = (KT / 32) * 4 * D / NT;
-  static constexpr int LDS_BYTES = 2 * (KTILEB + VTILEB);
+  static constexpr int MISCB = 2 * (KTILEB + VTILEB);  // per-wave key statistics for the exactness check
+  static constexpr int LDS_BYTES = MISCB + NW * (CH + 1) * 4;
   static_assert((KT * CH) % NT == 0, "tile chunks must divide evenly over the threads");
   static_assert(KT % 32 == 0, "key tile is a whole number of 32-key chunks");
   static_assert(CH == 16 || CH == 32, "a K row spans 16 or 32 lanes (d = 64 or 128)");
@@ -134,6 +136,10 @@ __device__ __forceinline__ float max_row16(float x) {
   x = fmaxf(x, dpp_f32<0x140>(x));  // row_mirror
   return x;
 }
+__device__ __forceinline__ float add_xor16_f32(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 // Largest value over the lane pair (l, l ^ 16) / (l, l ^ 32).
 __device__ __forceinline__ float max_xor16_f32(float x) {
   auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -173,6 +179,118 @@ __device__ __forceinline__ void slice5(f32x4 x, int e, uint32_t (&w)[5]) {
 #define HFA_F32_SKEW 1
 #endif
 
+// Workgroup barrier that waits only for this wave's LDS operations.
+__device__ __forceinline__ void lds_barrier_f32() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Largest bound on the error of an int8-slice score (natural-log units) that
+// a tile may have and keep the int8 products: 2^-22, so that with scores off
+// by at most this much, O moves by at most 2^-22 (max v - min v) and the
+// log-sum-exp by 2^-22 -- a small part of the 1e-5 budget.
+constexpr double kExactScoreBound = 0x1p-22;
+
+// Exact recomputation of one wave's query rows (16 QB rows from qrow0), for
+// waves whose int8-slice scores are not accurate enough (inputs whose rows mix
+// magnitudes far apart, so that a small entry of one row meets a large entry
+// of the other).  Everything comes straight from memory, no LDS and no
+// barrier; the same online normalisation, with both products on the fp64
+// matrix cores (v_mfma_f64_16x16x4_f64):
+//  * S^T = K Q^T per 16-key block: A row i reads key 4 (i % 4) + i / 4 of the
+//    block (the f64 product leaves register r of lane group g with output row
+//    4 r + g, so lane (i16, g) register r holds key 4 g + r for query i16);
+//    lane group g contracts the columns g d/4 .. g d/4 + d/4 - 1.  Each
+//    product of two fp32 values is exact in fp64, the sums are fp64.
+//  * The running max is in log2 units, rounded up to an integer, so rescale
+//    factors are exact powers of two; weights p = exp2 of the fp64 argument
+//    rounded to fp32 (as in the fast path), kept in fp64.
+//  * O^T += V^T P^T per 16-column block n: A = V[key 4 g + t][16 n + i16],
+//    B = the lane's own weight of key 4 g + t (register t), for t < 4; lane
+//    (i16, g) register r accumulates column 16 n + 4 r + g of query i16.
+template <int D, int QB>
+__device__ __forceinline__ void exact_rows_impl(const float* __restrict__ Qh, const float* __restrict__ Kh,
+                                                         const float* __restrict__ Vh, float* __restrict__ Oh,
+                                                         float* __restrict__ lse_h, int N, int qrow0, double c2,
+                                                         float qmul) {
+  constexpr int DQ = D / 4;
+  const int lane = threadIdx.x & 63;
+  const int i16 = lane & 15, g = lane >> 4;
+  const int pi = 4 * (i16 & 3) + (i16 >> 2);  // key of A row i16 within a 16-key block
+  f64x4 acc[QB][D / 16];
+  double m2[QB], l_run[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m2[qb] = -INFINITY;
+    l_run[qb] = 0.0;
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) acc[qb][n] = f64x4{0.0, 0.0, 0.0, 0.0};
+  }
+  for (int k0 = 0; k0 < N; k0 += 16) {
+    f64x4 s[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) s[qb] = f64x4{0.0, 0.0, 0.0, 0.0};
+    const float* krow = Kh + static_cast<size_t>(min(k0 + pi, N - 1)) * D + g * DQ;
+#pragma unroll 2
+    for (int t4 = 0; t4 < DQ / 4; ++t4) {
+      const f32x4 kf = *reinterpret_cast<const f32x4*>(krow + 4 * t4);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int row = min(qrow0 + 16 * qb + i16, N - 1);
+        const f32x4 qf = *reinterpret_cast<const f32x4*>(Qh + static_cast<size_t>(row) * D + g * DQ + 4 * t4) * qmul;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          s[qb] = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(kf[e]), static_cast<double>(qf[e]), s[qb],
+                                                       0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      double mx = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (k0 + 4 * g + r >= N) s[qb][r] = -INFINITY;
+        mx = fmax(mx, s[qb][r]);
+      }
+      mx = max_xor<32>(max_xor<16>(mx));
+      const double m_new = fmax(m2[qb], ceil(mx * c2));
+      const double alpha = __builtin_amdgcn_ldexp(1.0, static_cast<int>(fmax(m2[qb] - m_new, -1022.0)));
+      double p[4], ts = 0.0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        p[r] = static_cast<double>(exp2_hw(static_cast<float>(fma(s[qb][r], c2, -m_new))));
+        ts += p[r];
+      }
+      l_run[qb] = l_run[qb] * alpha + ts;
+      m2[qb] = m_new;
+#pragma unroll
+      for (int n = 0; n < D / 16; ++n) {
+        f64x4 a = acc[qb][n] * alpha;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float vv = Vh[static_cast<size_t>(min(k0 + 4 * g + t, N - 1)) * D + 16 * n + i16];
+          a = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(vv), p[t], a, 0, 0, 0);
+        }
+        acc[qb][n] = a;
+      }
+    }
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const double l_tot = add_xor<32>(add_xor<16>(l_run[qb]));
+    const int row = qrow0 + 16 * qb + i16;
+    if (row < N) {
+      float* orow = Oh + static_cast<size_t>(row) * D;
+#pragma unroll
+      for (int n = 0; n < D / 16; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) orow[16 * n + 4 * r + g] = static_cast<float>(acc[qb][n][r] / l_tot);
+      if (g == 0) lse_h[row] = static_cast<float>((m2[qb] + log2(l_tot)) * kLn2);
+    }
+  }
+}
+
 template <class T>
 __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
@@ -208,11 +326,14 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
   const float qmul = static_cast<float>(q_mode);
   u32x4 qs[QB][D / 64][T::NSL];
   int eq[QB];
+  // The wave's query statistics for the exactness check of each key tile:
+  // the largest 2^e_q and the largest L1 norm sum_c |q_c| over its rows.
+  float wave_b = 0.0f, wave_a = 0.0f;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qrow0 + qb * 16 + i16;
     f32x4 x[D / 64][4];
-    float mx = 0.0f;
+    float mx = 0.0f, l1 = 0.0f;
 #pragma unroll
     for (int h = 0; h < D / 64; ++h)
 #pragma unroll
@@ -222,9 +343,13 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
         v *= qmul;
         x[h][t4] = v;
         mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+        l1 += (fabsf(v[0]) + fabsf(v[1])) + (fabsf(v[2]) + fabsf(v[3]));
       }
     mx = max_xor32(max_xor16_f32(mx));
+    l1 = add_xor32(add_xor16_f32(l1));
     eq[qb] = row_exponent(mx);
+    if (mx > 0.0f) wave_b = fmaxf(wave_b, __builtin_amdgcn_ldexpf(1.0f, eq[qb]));
+    wave_a = fmaxf(wave_a, l1);
 #pragma unroll
     for (int h = 0; h < D / 64; ++h)
 #pragma unroll
@@ -235,6 +360,16 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
         for (int a2 = 0; a2 < T::NSL; ++a2) qs[qb][h][a2][t4] = w[a2];
       }
   }
+
+  // Every lane of a 16-lane row holds one query; the four rows hold the same
+  // queries, so a row reduction gives the wave's maxima (kept in scalar
+  // registers: they are only needed after the key loop).
+  wave_b = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(max_row16(wave_b))));
+  wave_a = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(max_row16(wave_a))));
+  // The largest exponent of the key rows this thread stages, and the largest
+  // L1 norm of its column chunk of them.
+  int kmax_e = -1024;
+  float kmax_a = 0.0f;
 
   f32x4 acc[QB][D / 16];
   double m2[QB], l_run[QB];
@@ -254,9 +389,15 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
   // full: tile j lies wholly below N (no key needs the bounds check).
   auto stage_load = [&](int j, auto full_tag) __attribute__((always_inline)) {
     constexpr bool full = decltype(full_tag)::value;
+    // In the 256-row tile, an opaque copy of the thread index, as in
+    // stage_store: the per-lane address parts are recomputed here instead of
+    // being spilled across the key loop (and reloaded inside it).  The other
+    // tilings have the registers to keep them.
+    int tid_here = tid;
+    if constexpr (T::QB >= 2) asm volatile("" : "+v"(tid_here));
 #pragma unroll
     for (int u = 0; u < T::LOADS; ++u) {
-      const int idx = tid + u * T::NT;
+      const int idx = tid_here + u * T::NT;
       const int row = idx / T::CH, ch = idx % T::CH;
       const int key = j * KT + row;
       u32x4 kx = {0u, 0u, 0u, 0u};
@@ -265,7 +406,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
     }
 #pragma unroll
     for (int it = 0; it < T::VITEMS; ++it) {
-      const int item = tid + it * T::NT;
+      const int item = tid_here + it * T::NT;
       const int vcol = item % D, cg = item / D;
       const int c = cg >> 2, g8 = cg & 3;
 #pragma unroll
@@ -281,26 +422,28 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
     // K rows as int8 slices under each row's own exponent.  The CH lanes
     // holding one row (16 or 32 consecutive lanes) agree on its largest
     // magnitude first.
-    // The thread index goes through an empty asm statement so that the LDS
-    // addresses below are recomputed here (a few shifts) rather than hoisted
-    // out of the key loop and spilled.
-    int tid_here = tid;
-    asm volatile("" : "+v"(tid_here));
 #pragma unroll
     for (int u = 0; u < T::LOADS; ++u) {
-      const int idx = tid_here + u * T::NT;
+      const int idx = tid + u * T::NT;
       const int row = idx / T::CH, ch = idx % T::CH;
       const f32x4 x = __builtin_bit_cast(f32x4, kreg[u]);
       float mx = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+      // this lane's part of the row's L1 norm (its column chunk is the same in
+      // every row it stages: ch = tid % CH)
+      kmax_a = fmaxf(kmax_a, (fabsf(x[0]) + fabsf(x[1])) + (fabsf(x[2]) + fabsf(x[3])));
       mx = max_row16(mx);
       if constexpr (T::CH == 32) mx = max_xor16_f32(mx);
       const int e = row_exponent(mx);
       uint32_t w[T::NSL];
       slice5(x, e, w);
+      // One opaque address for this lane's five slice stores (the planes are
+      // immediate offsets from it), recomputed here like the thread index.
+      int off0 = row * T::KSROW + 4 * ch;
+      asm volatile("" : "+v"(off0));
 #pragma unroll
-      for (int a2 = 0; a2 < T::NSL; ++a2)
-        *reinterpret_cast<uint32_t*>(kt + a2 * T::KSPLANEB + row * T::KSROW + 4 * ch) = w[a2];
-      if (ch == 0) *reinterpret_cast<int*>(kt + T::NSL * T::KSPLANEB + 4 * row) = e;
+      for (int a2 = 0; a2 < T::NSL; ++a2) *reinterpret_cast<uint32_t*>(kt + off0 + a2 * T::KSPLANEB) = w[a2];
+      if (ch == 0) *reinterpret_cast<int*>(kt + T::KEXPB + 4 * row) = e;
+      kmax_e = max(kmax_e, e);
     }
     // Split each V value into three bf16 pieces by truncation: x1 keeps the
     // top 16 bits of x, x2 the top 16 bits of x - x1, x3 = x - x1 - x2 (both
@@ -391,7 +534,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
 #pragma unroll
         for (int a2 = 0; a2 < T::NSL; ++a2)
           ks[h][a2] = __builtin_bit_cast(i32x4, lds_load16(kt, a2 * T::KSPLANEB + (kb * 16 + i16) * T::KSROW + 64 * h + 16 * g));
-      const i32x4 ek = __builtin_bit_cast(i32x4, lds_load16(kt, T::NSL * T::KSPLANEB + (kb * 16 + 4 * g) * 4));
+      const i32x4 ek = __builtin_bit_cast(i32x4, lds_load16(kt, T::KEXPB + (kb * 16 + 4 * g) * 4));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         i32x4 at[2 * T::NSL - 4];
@@ -418,6 +561,10 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
       }
     }
 
+    // ---- exact scores for a tile whose slice bound is too loose: fp64
+    // products of the fp32 values (exact) summed in fp64, read from memory
+    // (the tile was just staged, so it is in the caches).  Rare: the five
+    // evaluation workloads never take it.
     // ---- keys past the end get score -inf
     const int key0 = j * KT;
     if (!steady && key0 + KT > N) {
@@ -523,6 +670,51 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
   }
   for (; j < ntiles; ++j) tile_step(j, 0, std::false_type{});
 
+
+  // ---- exactness check.  The workgroup's largest key exponent, and a bound
+  // on its largest key L1 norm (the sum over the column chunks of each
+  // chunk's largest L1 norm, over every row staged by any thread), go through
+  // LDS; each wave bounds the error of its int8-slice scores with them and its
+  // own query statistics,
+  //   |ds| <= |scale| (2^-35 (2^e_k A_q + 2^e_q A_k) + d 2^-40 2^(e_q + e_k)),
+  // A = sum_c |x_c| of the row (the 2^-35 terms are the slicing residuals
+  // |r| <= 2^(e-35) against the other row's entries, the last the dropped
+  // slice products, a + b >= 6, below 3.02 d 2^-42 2^(e_q + e_k), with room
+  // for the fp64 combination and the residual products), here with the
+  // largest e and A of either side.  A wave whose bound exceeds
+  // kExactScoreBound recomputes its rows exactly.
+  {
+    // lanes l, l + CH, ... of a wave share a column chunk
+#pragma unroll
+    for (int m = 1; m < 64; m *= 2) {
+      kmax_e = max(kmax_e, __shfl_xor(kmax_e, m));
+      if (m >= T::CH) kmax_a = fmaxf(kmax_a, __shfl_xor(kmax_a, m));
+    }
+    int* kst = reinterpret_cast<int*>(smem + T::MISCB);
+    if (lane < T::CH) kst[wave * T::CH + lane] = __float_as_int(kmax_a);
+    if (lane == 0) kst[T::NW * T::CH + wave] = kmax_e;
+    lds_barrier_f32();
+    float ak = 0.0f;
+#pragma unroll
+    for (int c = 0; c < T::CH; ++c) {
+      float m = 0.0f;
+#pragma unroll
+      for (int w = 0; w < T::NW; ++w) m = fmaxf(m, __int_as_float(kst[w * T::CH + c]));
+      ak += m;
+    }
+    kmax_a = ak;
+#pragma unroll
+    for (int w = 0; w < T::NW; ++w) kmax_e = max(kmax_e, kst[T::NW * T::CH + w]);
+    const double abs_scale = c2 * kLn2;
+    const double bq = wave_b > 0.0f ? static_cast<double>(wave_b) : 0.0;
+    const double bk = __builtin_amdgcn_ldexp(1.0, kmax_e);
+    const double bound = abs_scale * (__builtin_amdgcn_ldexp(bk * wave_a + bq * kmax_a, -35) +
+                                      __builtin_amdgcn_ldexp(bq * bk, -40) * D);
+    if (bound > kExactScoreBound) {
+      exact_rows_impl<D, QB>(Qh, Kh, Vh, Oh, LSE + static_cast<size_t>(bh) * N, N, qrow0, c2, qmul);
+      return;
+    }
+  }
 
   // ---- epilogue.  acc[qb][n][r] is O[q][16n + 4g + r].
 #pragma unroll

@@ -17,9 +17,15 @@
  * the pages; it is the running max plus the log of the running denominator.
  *
  * Precision.  HFA_F32: fp32 in and out.  Q K^T is formed from exact int8
- * slices of each row of Q and K (five slices under a power of two above the
- * row's largest magnitude) on the int8 matrix cores, accumulated exactly and
- * combined in fp64: the score error is at most |scale| d 2^-32 max|q| max|k|.
+ * slices of each row of Q and K (five slices under a power of two 2^e above
+ * the row's largest magnitude) on the int8 matrix cores, accumulated exactly
+ * and combined in fp64.  The score error of that route is bounded per pair of
+ * rows by |scale| (2^-35 (2^e_k A_q + 2^e_q A_k) + d 2^-40 2^(e_q + e_k)),
+ * A = sum_c |x_c| of the row; each workgroup evaluates this bound for every
+ * key against its own query rows, and if any key exceeds 2^-22 (rows that mix
+ * magnitudes far apart, e.g. outlier channels) the workgroup recomputes its
+ * rows with both products on the fp64 matrix cores instead (exact products,
+ * fp64 sums), so the int8 route serves only where it is within 2^-22.
  * P V runs on the bf16 matrix cores from exact three-piece bf16 splits of P
  * and V (six of the nine piece products; each dropped one is below 2^-21 of
  * its |p v| term) with fp32 accumulation; exp2 runs in fp32 and the

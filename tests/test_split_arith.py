@@ -152,3 +152,99 @@ def test_three_piece_splits_exact():
     Vt.append((vv - Vt[0] - Vt[1]).astype(F))
     dropped = sum(P[a].astype(np.float64) * Vt[b] for a in range(3) for b in range(3) if a + b >= 3)
     assert np.all(np.abs(dropped) <= 2.0 ** -21 * np.abs(pp.astype(np.float64) * vv))
+
+
+# ---- the exactness check that sends a workgroup to exact fp64 scores --------
+
+EXACT_SCORE_BOUND = 2.0 ** -22  # largest slice-score error bound kept on the int8 path
+
+
+def slice_scores(q: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """The int8-slice scores q . k^T the kernel forms (19 slice products, fp64 combination)."""
+    eq = row_exponent(np.abs(q).max(axis=1))
+    ek = row_exponent(np.abs(k).max(axis=1))
+    sq, _ = slice5(q, eq)
+    sk, _ = slice5(k, ek)
+    acc = [sum(sq[a] @ sk[b].T for a in range(5) for b in range(5) if a + b == t) for t in range(6)]
+    comb = sum(a_.astype(np.float64) * 2.0 ** (-7 * t) for t, a_ in enumerate(acc))
+    return np.ldexp(comb, eq[:, None] + ek[None, :] - 12)
+
+
+def pair_bound(q: np.ndarray, k: np.ndarray) -> np.ndarray:
+    """|ds| <= 2^-35 (2^e_k A_q + 2^e_q A_k) + d 2^-40 2^(e_q + e_k) per (query, key), A = L1 norm."""
+    d = q.shape[1]
+    bq = np.where(np.abs(q).max(axis=1) > 0, np.ldexp(1.0, row_exponent(np.abs(q).max(axis=1))), 0.0)
+    bk = np.ldexp(1.0, row_exponent(np.abs(k).max(axis=1)))
+    aq = np.abs(q.astype(np.float64)).sum(axis=1)
+    ak = np.abs(k.astype(np.float64)).sum(axis=1)
+    return 2.0 ** -35 * (bk[None, :] * aq[:, None] + bq[:, None] * ak[None, :]) + d * 2.0 ** -40 * np.outer(bq, bk)
+
+
+def wave_flag(q: np.ndarray, k: np.ndarray, scale: float) -> bool:
+    """The kernel's check for one wave (its query rows q) after the key loop: the largest
+    L1 norm and 2^e over the wave's query rows, the largest 2^e over every key row of the
+    head (the workgroup stages them all), and for the keys' L1 norm the sum over the
+    4-column chunks of each chunk's largest L1 norm; combined into one bound."""
+    d = q.shape[1]
+    mq = np.abs(q).max(axis=1)
+    bq = float(np.max(np.where(mq > 0, np.ldexp(1.0, row_exponent(mq)), 0.0)))
+    aq = float(np.abs(q.astype(np.float64)).sum(axis=1).max())
+    bk = float(np.ldexp(1.0, row_exponent(np.abs(k).max(axis=1)).max()))
+    ak = float(np.abs(k.astype(np.float64)).reshape(k.shape[0], d // 4, 4).sum(axis=2).max(axis=0).sum())
+    assert ak >= np.abs(k.astype(np.float64)).sum(axis=1).max()
+    bound = abs(scale) * (2.0 ** -35 * (bk * aq + bq * ak) + d * 2.0 ** -40 * bq * bk)
+    return bound > EXACT_SCORE_BOUND
+
+
+def outlier_rows(rng, n, d, small, big, channel):
+    """Rows of N(0, small^2) entries with one outlier channel of magnitude ~big."""
+    x = rng.standard_normal((n, d)) * small
+    x[:, channel] = big * np.where(rng.random(n) < 0.5, -1.0, 1.0) * (1 + rng.random(n))
+    return x.astype(F)
+
+
+@pytest.mark.parametrize("spread", [0, 10, 24])
+@pytest.mark.parametrize("d", [64, 128])
+def test_pair_bound_covers_the_slice_error(spread, d):
+    rng = np.random.default_rng(2000 * d + spread)
+    q = random_rows(rng, 64, d, spread)
+    k = random_rows(rng, 64, d, spread)
+    k[:8] = outlier_rows(rng, 8, d, 1e-3, 1e4, 3)
+    q[:8] = outlier_rows(rng, 8, d, 1e-3, 1e3, 7)
+    err = np.abs(slice_scores(q, k) - q.astype(np.float64) @ k.astype(np.float64).T)
+    assert np.all(err <= pair_bound(q, k))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_outlier_channels_take_the_exact_path(d):
+    # q rows: entries ~1e-3 with an outlier channel ~1e3; k rows: entries ~1e-3
+    # with another outlier channel ~1e4.  The small q entry on k's outlier
+    # channel is held to 2^(10-35) only, so the slice scores miss by far more
+    # than the 1e-5 budget allows -- and the check sends the workgroup to the
+    # exact scores.
+    rng = np.random.default_rng(d)
+    scale = 1.0 / np.sqrt(d)
+    q = outlier_rows(rng, 256, d, 1e-3, 1e3, 5)
+    k = outlier_rows(rng, 256, d, 1e-3, 1e4, 11)
+    err = scale * np.abs(slice_scores(q, k) - q.astype(np.float64) @ k.astype(np.float64).T)
+    assert err.max() > 2e-5
+    assert wave_flag(q, k, scale)
+    # plain sequential fp32 dot products stay far below it on the same rows
+    fp32 = np.zeros((q.shape[0], k.shape[0]), dtype=F)
+    for c in range(d):
+        fp32 = (fp32 + (q[:, c:c + 1] * k[None, :, c]).astype(F)).astype(F)
+    assert scale * np.abs(fp32 - q.astype(np.float64) @ k.astype(np.float64).T).max() < 2e-5
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3])
+def test_evaluation_workloads_stay_on_the_int8_path(cfg):
+    # With the head-wide maxima of the query statistics (at least those of any
+    # wave), the fp32 evaluation workloads stay below the bound: every wave
+    # keeps the int8 products.
+    from fa2_fwd_amd import workloads as W
+
+    w = W.CONFIGS[cfg]
+    q, k, _ = (t.numpy() for t in W.workload_inputs(w))
+    for b in range(w.B):
+        for h in range(w.H):
+            assert not wave_flag(q[b, h], k[b, h], w.scale), (b, h)
