@@ -32,9 +32,11 @@ HFA_ERR_ALIAS = 6
 HFA_ERR_NO_DEVICE = 7
 HFA_ERR_LAUNCH = 8
 HFA_ERR_EPS = 9
+HFA_ERR_WORKSPACE = 10
 
-EXPORTED = ("hfa_attn_fwd", "hfa_status_str", "hfa_block_rows", "hfa_attn_fwd_graph_create", "hfa_graph_launch",
-            "hfa_graph_destroy", "hfa_softmax_rows", "hfa_rmsnorm")
+EXPORTED = ("hfa_attn_fwd", "hfa_status_str", "hfa_block_rows", "hfa_key_splits", "hfa_attn_fwd_workspace_size",
+            "hfa_attn_fwd_split", "hfa_attn_fwd_graph_create", "hfa_graph_launch", "hfa_graph_destroy",
+            "hfa_softmax_rows", "hfa_rmsnorm")
 
 _lib = None
 
@@ -67,6 +69,13 @@ def load_library(path: str | Path | None = None) -> ctypes.CDLL:
     lib.hfa_status_str.restype = ctypes.c_char_p
     lib.hfa_block_rows.argtypes = [ctypes.c_int, i64, i64, i64, i64]
     lib.hfa_block_rows.restype = i64
+    lib.hfa_key_splits.argtypes = [ctypes.c_int, i64, i64, i64, i64]
+    lib.hfa_key_splits.restype = i64
+    lib.hfa_attn_fwd_workspace_size.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64]
+    lib.hfa_attn_fwd_workspace_size.restype = i64
+    lib.hfa_attn_fwd_split.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int, i64, vp,
+                                       i64, vp]
+    lib.hfa_attn_fwd_split.restype = ctypes.c_int
     lib.hfa_attn_fwd_graph_create.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
                                               i64, ctypes.POINTER(vp)]
     lib.hfa_attn_fwd_graph_create.restype = ctypes.c_int
@@ -94,6 +103,20 @@ def hfa_status_str(status: int) -> str:
 
 def hfa_block_rows(dtype: int, B: int, H: int, N: int, d: int) -> int:
     return int(load_library().hfa_block_rows(int(dtype), int(B), int(H), int(N), int(d)))
+
+
+def hfa_key_splits(dtype: int, B: int, H: int, N: int, d: int) -> int:
+    return int(load_library().hfa_key_splits(int(dtype), int(B), int(H), int(N), int(d)))
+
+
+def hfa_attn_fwd_workspace_size(dtype: int, B: int, H: int, N: int, d: int, splits: int) -> int:
+    return int(load_library().hfa_attn_fwd_workspace_size(int(dtype), int(B), int(H), int(N), int(d), int(splits)))
+
+
+def hfa_attn_fwd_split(q, k, v, o, lse, B, H, N, d, scale, dtype, splits, workspace, workspace_bytes, stream) -> int:
+    """Raw C-ABI call: pointers as ints (device addresses) or None; returns the status."""
+    return load_library().hfa_attn_fwd_split(q, k, v, o, lse, B, H, N, d, scale, dtype, splits, workspace,
+                                             workspace_bytes, stream)
 
 
 def hfa_attn_fwd_graph_create(q, k, v, o, lse, B, H, N, d, scale, dtype, count):
@@ -232,22 +255,42 @@ def _stream_handle(stream, device):
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
-def attn_fwd(q, k, v, scale: float | None = None, out=None, lse=None, stream=None):
+def attn_fwd(q, k, v, scale: float | None = None, out=None, lse=None, stream=None, splits: int = 0,
+             workspace=None):
     """O, LSE = attention forward of device tensors q, k, v of shape [B, H, N, d].
 
     ``scale`` defaults to 1/sqrt(d).  ``out`` ([B,H,N,d], q's dtype) and ``lse``
-    ([B,H,N] float32) may be given to write into caller buffers.  The kernel is
+    ([B,H,N] float32) may be given to write into caller buffers.  The kernels are
     enqueued on ``stream`` (default: torch's current stream) and not waited for.
-    Raises ValueError on dtype, shape, device or contiguity mismatch and
-    HfaError on a library error.
+    ``splits`` is the key split (hfa_attn_fwd_split): 0 lets the library choose (bf16
+    shapes too small to fill the GPU split their keys), 1 never splits.  A split call
+    needs a workspace of hfa_attn_fwd_workspace_size bytes: ``workspace`` (a device
+    tensor) if given, else one from torch's allocator, kept alive for ``stream``.
+    Raises ValueError on dtype, shape, device or contiguity mismatch and HfaError on a
+    library error.
     """
     import torch
 
     B, H, N, d, code, scale, out, lse = _prepare(q, k, v, scale, out, lse)
     handle = _stream_handle(stream, q.device)
+    need = hfa_attn_fwd_workspace_size(code, B, H, N, d, int(splits))
+    if need < 0:
+        raise HfaError(HFA_ERR_UNSUPPORTED if int(splits) >= 0 else HFA_ERR_SHAPE)
     with torch.cuda.device(q.device):
-        st = hfa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                          B, H, N, d, scale, code, handle)
+        if need == 0:
+            st = hfa_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                              B, H, N, d, scale, code, handle)
+        else:
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+                if stream is not None:
+                    workspace.record_stream(stream if isinstance(stream, torch.cuda.Stream)
+                                            else torch.cuda.ExternalStream(handle, device=q.device))
+            elif not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or workspace.device != q.device:
+                raise ValueError("workspace must be a tensor on q's device")
+            st = hfa_attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                    B, H, N, d, scale, code, int(splits), workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), handle)
     if st != HFA_OK:
         raise HfaError(st)
     return out, lse

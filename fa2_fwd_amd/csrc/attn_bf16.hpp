@@ -186,11 +186,25 @@ __device__ __forceinline__ void vmcnt_wait() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <class T>
+// Key split.  With SPLIT, the keys of each (batch, head) are cut into
+// `nsplit` ranges of `split_tiles` key tiles; workgroup (bh, split, q-tile)
+// runs the same loop over its range only and writes, instead of O and LSE,
+// its partial result: the range's normalised output O_s = acc / l (fp32) to
+// part_o[split][bh][row][:] and its log-sum-exp in log2 units, m2 + log2 l,
+// to part_lse[split][bh][row].  attn_merge_bf16_kernel combines the ranges
+// by the same identity as the running update.
+struct SplitArgs {
+  int nsplit;       // key ranges per head (1: no split)
+  int split_tiles;  // key tiles per range
+  float* part_o;    // [nsplit][BH][N][D]
+  float* part_lse;  // [nsplit][BH][N]
+};
+
+template <class T, bool SPLIT>
 __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int N, int n_qt, int total_wg, float c2,
-    int q_mode) {
+    int q_mode, SplitArgs sa) {
   constexpr int D = T::D, QB = T::QB, KT = T::KT, ROWB = T::ROWB, TILEB = T::TILEB;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* const kbuf = smem;                    // K ring: NBUF tile buffers
@@ -202,12 +216,20 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   const int grp = wave >> 2;  // ping-pong group; waves w and w + 4 share a SIMD
   const int i32 = lane & 31, hh = lane >> 5;
 
+  // Logical tile order: q-tile fastest, then the key range, then the head,
+  // so that the workgroups sharing a head's key range are neighbours (and,
+  // after xcd_remap, on one XCD).
   const int tile = xcd_remap(blockIdx.x, total_wg);
-  const int bh = tile / n_qt, qt = tile - bh * n_qt;
+  const int grp_id = tile / n_qt, qt = tile - grp_id * n_qt;
+  const int sp = SPLIT ? grp_id % sa.nsplit : 0;
+  const int bh = SPLIT ? grp_id / sa.nsplit : grp_id;
   const size_t head = static_cast<size_t>(bh) * static_cast<size_t>(N) * D;
+  // This workgroup's keys: [key_begin, key_begin + nkeys).
+  const int key_begin = SPLIT ? sp * sa.split_tiles * KT : 0;
+  const int nkeys = SPLIT ? min(N - key_begin, sa.split_tiles * KT) : N;
   const __bf16* Qh = Q + head;
-  const __bf16* Kh = K + head;
-  const __bf16* Vh = V + head;
+  const __bf16* Kh = K + head + static_cast<size_t>(key_begin) * D;
+  const __bf16* Vh = V + head + static_cast<size_t>(key_begin) * D;
   __bf16* Oh = O + head;
   const int qrow0 = qt * T::BR + wave * T::WQ;
 
@@ -253,7 +275,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
       for (int r = 0; r < 16; ++r) acc[qb][n][r] = 0.0f;
   }
 
-  const int ntiles = (N + KT - 1) / KT;
+  const int ntiles = (nkeys + KT - 1) / KT;
 
   // ---- K/V streaming: HBM -> LDS directly (global_load_lds_dwordx4), no
   // registers.  Group 0 streams the K tiles, group 1 the V tiles, each into a
@@ -290,11 +312,11 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
     if (!steady && t >= ntiles) return;
     char* dst = stream_ring + slot_of(t, slot) * TILEB;
     const char* tile_src = reinterpret_cast<const char*>(stream_src + static_cast<size_t>(t) * KT * D);
-    if (steady || (t + 1) * KT <= N) {
+    if (steady || (t + 1) * KT <= nkeys) {
 #pragma unroll
       for (int u = 0; u < T::LD; ++u) dma16(tile_src, dma_off[u], dst + (wig * T::LD + u) * 1024);
     } else {  // ragged last tile: rows past the end re-read the last row
-      const int last = N - 1 - t * KT;
+      const int last = nkeys - 1 - t * KT;
 #pragma unroll
       for (int u = 0; u < T::LD; ++u) {
         const int row = ((wig * T::LD + u) * 64 + lane) / T::CH;
@@ -450,15 +472,15 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   // rare, wave-uniform branch).  Every weight stays <= kSumLimit either way.
   auto softmax = [&](int j, auto first_tag, auto steady_tag) __attribute__((always_inline)) {
     constexpr bool first = decltype(first_tag)::value;
-    constexpr bool steady = decltype(steady_tag)::value;  // tile j is not the last: no key past N
+    constexpr bool steady = decltype(steady_tag)::value;  // tile j is not the last: no key past nkeys
     const int key0 = j * KT;
-    if (!steady && key0 + KT > N) {  // keys past the end of the sequence get score -inf (weight 0)
+    if (!steady && key0 + KT > nkeys) {  // keys past the end of the range get score -inf (weight 0)
 #pragma unroll
       for (int kb = 0; kb < KT / 32; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = key0 + kb * 32 + 16 * (r >> 3) + 8 * hh + (r & 7);
-          if (key >= N)
+          if (key >= nkeys)
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) s[qb][kb][r] = -INFINITY;
         }
@@ -668,6 +690,31 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   wave_prio(false);
   if (grp == 0) lds_barrier();  // both groups execute the same number of barriers
 
+  // ---- epilogue of a key range: its normalised output and log-sum-exp
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float l_tot = add_xor32(l_run[qb]);
+      const float inv = 1.0f / l_tot;
+      const int row = qrow0 + qb * 32 + i32;
+      if (row < N) {
+        const size_t prow = (static_cast<size_t>(sp) * (total_wg / (n_qt * sa.nsplit)) + bh) * N + row;
+        float* orow = sa.part_o + prow * D;
+#pragma unroll
+        for (int n = 0; n < D / 32; ++n)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            f32x4 o4;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) o4[b] = acc[qb][n][4 * a + b] * inv;
+            *reinterpret_cast<f32x4*>(orow + 32 * n + 8 * a + 4 * hh) = o4;
+          }
+        if (hh == 0) sa.part_lse[prow] = m2[qb] + log2f(l_tot);
+      }
+    }
+    return;
+  }
+
   // ---- epilogue: normalise, round to bf16, one write of O and of LSE
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -692,6 +739,44 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
       }
     }
   }
+}
+
+// Combines the key ranges of a split launch, one query row per group of
+// D/8 threads (8 columns each): with lse_s = m2_s + log2 l_s of range s
+// (log2 units), M = max_s lse_s and w_s = 2^(lse_s - M),
+//     O = sum_s w_s O_s / sum_s w_s,    LSE = ln 2 (M + log2 sum_s w_s),
+// the identity of the running update applied to whole ranges.  O is rounded
+// to bf16 once; the log-sum-exp is combined in fp64.
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_bf16_kernel(const float* __restrict__ part_o,
+                                                              const float* __restrict__ part_lse,
+                                                              __bf16* __restrict__ O, float* __restrict__ LSE,
+                                                              int rows, int nsplit) {
+  constexpr int TPR = D / 8;  // threads per row
+  const int row = blockIdx.x * (256 / TPR) + static_cast<int>(threadIdx.x) / TPR;
+  const int c0 = (static_cast<int>(threadIdx.x) % TPR) * 8;
+  if (row >= rows) return;
+  float m = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) m = fmaxf(m, part_lse[static_cast<size_t>(s) * rows + row]);
+  float wsum = 0.0f;
+  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < nsplit; ++s) {
+    const size_t pr = static_cast<size_t>(s) * rows + row;
+    const float w = exp2_hw(part_lse[pr] - m);
+    const f32x4* src = reinterpret_cast<const f32x4*>(part_o + pr * D + c0);
+    a0 += w * src[0];
+    a1 += w * src[1];
+    wsum += w;
+  }
+  const float inv = 1.0f / wsum;
+  bf16x8 o8;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    o8[e] = static_cast<__bf16>(a0[e] * inv);
+    o8[4 + e] = static_cast<__bf16>(a1[e] * inv);
+  }
+  *reinterpret_cast<bf16x8*>(O + static_cast<size_t>(row) * D + c0) = o8;
+  if (c0 == 0) LSE[row] = static_cast<float>((static_cast<double>(m) + log2(static_cast<double>(wsum))) * kLn2);
 }
 
 }  // namespace hfa

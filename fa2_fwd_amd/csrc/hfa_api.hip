@@ -2,6 +2,7 @@
 // argument validation, device check, kernel dispatch and graph capture.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -87,25 +88,84 @@ ScaleArgs split_scale(float scale) {
   return {std::fabs(s) * kLog2e, s < 0 ? -1 : 1};
 }
 
+// Key split of a bf16 launch: `nsplit` ranges of `tiles` key tiles each
+// (every range non-empty); nsplit == 1 is the plain launch.
+struct KeySplit {
+  int64_t nsplit;
+  int64_t tiles;
+};
+constexpr int64_t kKeyTile = 64;   // keys per K/V tile of the bf16 kernel
+constexpr int64_t kMaxSplits = 32;
+
+KeySplit make_split(int64_t N, int64_t want) {
+  const int64_t ntiles = (N + kKeyTile - 1) / kKeyTile;
+  const int64_t s = std::max<int64_t>(1, std::min<int64_t>({want, ntiles, kMaxSplits}));
+  const int64_t tiles = (ntiles + s - 1) / s;
+  return {(ntiles + tiles - 1) / tiles, tiles};
+}
+
+// The split hfa_attn_fwd_split chooses when asked for none in particular:
+// shapes whose 256-row tiles give fewer workgroups than compute units split
+// their keys into as many ranges as still fit one round of workgroups on the
+// compute units, each range at least kMinSplitTiles key tiles long (shorter
+// ranges lose more to the partial results' round trip through memory and the
+// per-workgroup start-up than they gain; measured on the device).
+constexpr int64_t kMinSplitTiles = 32;
+int64_t auto_splits(hfa_dtype dtype, int64_t BH, int64_t N, int64_t d) {
+  if (dtype != HFA_BF16) return 1;
+  const int64_t br = d == 128 ? Bf16D128::BR : Bf16D64::BR;
+  const int64_t grid = BH * ((N + br - 1) / br);
+  if (grid >= kComputeUnits) return 1;
+  const int64_t ntiles = (N + kKeyTile - 1) / kKeyTile;
+  const int64_t want = std::min<int64_t>(kComputeUnits / grid, ntiles / kMinSplitTiles);
+  return want < 2 ? 1 : make_split(N, want).nsplit;
+}
+
+// Workspace bytes of a split launch: the partial outputs [nsplit][BH][N][d]
+// fp32, then the partial log-sum-exps [nsplit][BH][N] fp32.
+int64_t split_workspace_bytes(int64_t nsplit, int64_t BH, int64_t N, int64_t d) {
+  return nsplit <= 1 ? 0 : nsplit * BH * N * (d + 1) * 4;
+}
+
 // With launch == false only the one-time kernel attributes are set (before a
-// stream capture, which must contain nothing but the launches).
+// stream capture, which must contain nothing but the launches).  A split
+// launch (ks.nsplit > 1) writes its partial results to `work` and merges them
+// into o and lse with a second kernel.
 template <class T>
 hfa_status launch_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH,
-                       int64_t N, float scale, hipStream_t stream, bool launch) {
-  static std::once_flag flag;
-  static hipError_t err = hipSuccess;
-  auto kernel = attn_fwd_bf16_kernel<T>;
+                       int64_t N, float scale, hipStream_t stream, bool launch, KeySplit ks = {1, 0},
+                       void* work = nullptr) {
+  static std::once_flag flag, flag_split;
+  static hipError_t err = hipSuccess, err_split = hipSuccess;
+  auto kernel = attn_fwd_bf16_kernel<T, false>;
+  auto kernel_split = attn_fwd_bf16_kernel<T, true>;
   if (ensure_lds(kernel, T::LDS_BYTES, flag, err) != HFA_OK) return HFA_ERR_LAUNCH;
+  if (ensure_lds(kernel_split, T::LDS_BYTES, flag_split, err_split) != HFA_OK) return HFA_ERR_LAUNCH;
   if (!launch) return HFA_OK;
   const int64_t n_qt = (N + T::BR - 1) / T::BR;
-  const int64_t total = BH * n_qt;
-  if (total > INT_MAX) return HFA_ERR_SHAPE;
+  const int64_t total = BH * n_qt * ks.nsplit;
+  if (total > INT_MAX || BH * N > INT_MAX) return HFA_ERR_SHAPE;
   const ScaleArgs sa = split_scale(scale);
-  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(total)), dim3(T::NT), T::LDS_BYTES, stream,
-                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
+  SplitArgs sp{static_cast<int>(ks.nsplit), static_cast<int>(ks.tiles), nullptr, nullptr};
+  if (ks.nsplit > 1) {
+    sp.part_o = static_cast<float*>(work);
+    sp.part_lse = sp.part_o + ks.nsplit * BH * N * T::D;
+  }
+  hipLaunchKernelGGL((ks.nsplit > 1 ? kernel_split : kernel), dim3(static_cast<unsigned>(total)), dim3(T::NT),
+                     T::LDS_BYTES, stream, static_cast<const __bf16*>(q), static_cast<const __bf16*>(k),
                      static_cast<const __bf16*>(v), static_cast<__bf16*>(o), lse, static_cast<int>(N),
-                     static_cast<int>(n_qt), static_cast<int>(total), static_cast<float>(sa.c2), sa.q_mode);
-  return hipGetLastError() == hipSuccess ? HFA_OK : HFA_ERR_LAUNCH;
+                     static_cast<int>(n_qt), static_cast<int>(total), static_cast<float>(sa.c2), sa.q_mode, sp);
+  if (hipGetLastError() != hipSuccess) return HFA_ERR_LAUNCH;
+  if (ks.nsplit > 1) {
+    const int64_t rows = BH * N;
+    constexpr int64_t rows_per_block = 256 / (T::D / 8);
+    hipLaunchKernelGGL(attn_merge_bf16_kernel<T::D>, dim3(static_cast<unsigned>((rows + rows_per_block - 1) /
+                                                                                  rows_per_block)),
+                       dim3(256), 0, stream, sp.part_o, sp.part_lse, static_cast<__bf16*>(o), lse,
+                       static_cast<int>(rows), static_cast<int>(ks.nsplit));
+    if (hipGetLastError() != hipSuccess) return HFA_ERR_LAUNCH;
+  }
+  return HFA_OK;
 }
 
 template <class T>
@@ -153,11 +213,13 @@ hfa_status validate(const void* q, const void* k, const void* v, const void* o, 
 }
 
 // Kernel selection for a validated call; enqueues it on `stream` when launch.
+// ks / work: the key split of a bf16 call and its workspace.
 hfa_status dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t N,
-                    int64_t d, float scale, hfa_dtype dtype, hipStream_t st, bool launch) {
+                    int64_t d, float scale, hfa_dtype dtype, hipStream_t st, bool launch, KeySplit ks = {1, 0},
+                    void* work = nullptr) {
   if (dtype == HFA_BF16) {
-    if (d == 128) return launch_bf16<Bf16D128>(q, k, v, o, lse, BH, N, scale, st, launch);
-    return launch_bf16<Bf16D64>(q, k, v, o, lse, BH, N, scale, st, launch);
+    if (d == 128) return launch_bf16<Bf16D128>(q, k, v, o, lse, BH, N, scale, st, launch, ks, work);
+    return launch_bf16<Bf16D64>(q, k, v, o, lse, BH, N, scale, st, launch, ks, work);
   }
   if (d == 64) {
     switch (f32_d64_tiling(BH, N)) {
@@ -203,6 +265,7 @@ const char* hfa_status_str(hfa_status s) {
     case HFA_ERR_NO_DEVICE: return "no current gfx950 HIP device";
     case HFA_ERR_LAUNCH: return "kernel launch failed";
     case HFA_ERR_EPS: return "eps must be finite and > 0";
+    case HFA_ERR_WORKSPACE: return "workspace smaller than the key split needs";
     default: break;
   }
   return "unknown status";
@@ -215,6 +278,49 @@ hfa_status hfa_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
   const hfa_status dev = check_device();
   if (dev != HFA_OK) return dev;
   return dispatch(q, k, v, o, lse, B * H, N, d, scale, dtype, static_cast<hipStream_t>(stream), true);
+}
+
+int64_t hfa_key_splits(hfa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t d) {
+  if ((dtype != HFA_F32 && dtype != HFA_BF16) || (d != 64 && d != 128)) return 0;
+  if (B < 1 || H < 1 || N < 1 || B > INT64_MAX / H || N > INT_MAX / d) return 0;
+  return auto_splits(dtype, B * H, N, d);
+}
+
+int64_t hfa_attn_fwd_workspace_size(hfa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t d, int64_t splits) {
+  if ((dtype != HFA_F32 && dtype != HFA_BF16) || (d != 64 && d != 128)) return -1;
+  if (B < 1 || H < 1 || N < 1 || B > INT64_MAX / H || N > INT_MAX / d || splits < 0) return -1;
+  if (B * H > INT_MAX / N) return -1;
+  if (splits == 0) splits = auto_splits(dtype, B * H, N, d);
+  if (dtype != HFA_BF16 && splits > 1) return -1;
+  return split_workspace_bytes(make_split(N, splits).nsplit, B * H, N, d);
+}
+
+hfa_status hfa_attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                              int64_t H, int64_t N, int64_t d, float scale, hfa_dtype dtype, int64_t splits,
+                              void* workspace, int64_t workspace_bytes, void* stream) {
+  const hfa_status st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype);
+  if (st != HFA_OK) return st;
+  if (splits < 0) return HFA_ERR_SHAPE;
+  const int64_t BH = B * H;
+  if (BH > INT_MAX / N) return HFA_ERR_SHAPE;
+  if (splits == 0) splits = auto_splits(dtype, BH, N, d);
+  if (dtype != HFA_BF16 && splits > 1) return HFA_ERR_UNSUPPORTED;
+  const KeySplit ks = make_split(N, splits);
+  if (ks.nsplit > 1) {
+    const int64_t need = split_workspace_bytes(ks.nsplit, BH, N, d);
+    if (!workspace) return HFA_ERR_NULL;
+    if (misaligned(workspace, 16)) return HFA_ERR_ALIGN;
+    if (workspace_bytes < need) return HFA_ERR_WORKSPACE;
+    const size_t bytes = static_cast<size_t>(BH) * static_cast<size_t>(N) * static_cast<size_t>(d) * 2;
+    const size_t lse_bytes = static_cast<size_t>(BH) * static_cast<size_t>(N) * 4;
+    const size_t wb = static_cast<size_t>(need);
+    if (overlaps(workspace, wb, q, bytes) || overlaps(workspace, wb, k, bytes) || overlaps(workspace, wb, v, bytes) ||
+        overlaps(workspace, wb, o, bytes) || overlaps(workspace, wb, lse, lse_bytes))
+      return HFA_ERR_ALIAS;
+  }
+  const hfa_status dev = check_device();
+  if (dev != HFA_OK) return dev;
+  return dispatch(q, k, v, o, lse, BH, N, d, scale, dtype, static_cast<hipStream_t>(stream), true, ks, workspace);
 }
 
 hfa_status hfa_attn_fwd_graph_create(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -76,6 +76,7 @@ typedef enum {
   HFA_ERR_NO_DEVICE = 7,   /* no HIP device is current, or it is not gfx950 */
   HFA_ERR_LAUNCH = 8,      /* the kernel launch itself failed */
   HFA_ERR_EPS = 9,         /* hfa_rmsnorm: eps is not a finite value > 0 */
+  HFA_ERR_WORKSPACE = 10,  /* hfa_attn_fwd_split: workspace_bytes below what the split needs */
   HFA_STATUS_RANGE_MIN_ = -2147483647 - 1,
   HFA_STATUS_RANGE_MAX_ = 2147483647
 } hfa_status;
@@ -109,6 +110,49 @@ const char* hfa_status_str(hfa_status s);
  * head dim or a shape with B, H or N below 1.  Needs no device and makes no
  * HIP call. */
 int64_t hfa_block_rows(hfa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t d);
+
+/* Key split for shapes with few query tiles.  When B * H * ceil(N / B_r)
+ * row tiles give fewer workgroups than the GPU has compute units, the keys of
+ * each head can be cut into `splits` contiguous ranges (whole 64-key tiles),
+ * one workgroup per (row tile, range): each range runs the same online
+ * normalisation over its keys and leaves a partial result (its normalised
+ * output O_s and log-sum-exp L_s, fp32) in the caller's workspace, and a
+ * second kernel merges the ranges with the identity of the running update of
+ * neuralmasteryai "Hardware Acceleration & Custom Kernels", section 2, step 2,
+ * applied to whole ranges: with M = max_s L_s and w_s = exp(L_s - M),
+ * O = sum_s w_s O_s / sum_s w_s and LSE = M + log sum_s w_s.  bf16 only.
+ *
+ * hfa_key_splits: the split hfa_attn_fwd_split takes for splits == 0 (1: none;
+ * always 1 for HFA_F32); 0 for invalid arguments.  No device, no HIP call. */
+int64_t hfa_key_splits(hfa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t d);
+
+/* Workspace bytes hfa_attn_fwd_split needs for `splits` ranges (0: the
+ * automatic choice); 0 when the call splits nothing.  The requested count is
+ * clamped to [1, min(ceil(N / 64), 32)] and every range is non-empty, so the
+ * ranges actually used may be fewer.  -1 for invalid arguments (and for
+ * splits > 1 with HFA_F32).  No device, no HIP call. */
+int64_t hfa_attn_fwd_workspace_size(hfa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t d,
+                                    int64_t splits);
+
+/* hfa_attn_fwd with an optional key split.
+ *
+ *   q ... dtype, stream  as for hfa_attn_fwd, validated the same way first.
+ *   splits           key ranges per head: 0 = hfa_key_splits' choice, 1 = none
+ *                    (the call is then exactly hfa_attn_fwd), > 1 bf16 only
+ *                    (HFA_ERR_UNSUPPORTED for HFA_F32); < 0 is HFA_ERR_SHAPE.
+ *   workspace        device memory of at least workspace_bytes >=
+ *                    hfa_attn_fwd_workspace_size(dtype, B, H, N, d, splits)
+ *                    bytes, 16-byte aligned, overlapping no other argument;
+ *                    may be NULL when that size is 0.  Its contents on entry
+ *                    do not matter; the call leaves the partial results there.
+ *
+ * Errors, before any HIP call: those of hfa_attn_fwd, then HFA_ERR_NULL (no
+ * workspace), HFA_ERR_ALIGN, HFA_ERR_WORKSPACE (too small), HFA_ERR_ALIAS.
+ * Asynchronous on `stream` (two kernels in stream order); the library
+ * allocates nothing.  Calls that share a workspace must not overlap in time. */
+hfa_status hfa_attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int64_t B, int64_t H, int64_t N, int64_t d, float scale, hfa_dtype dtype,
+                              int64_t splits, void* workspace, int64_t workspace_bytes, void* stream);
 
 /* Graph replay for launch-bound shapes.  Following the "CUDA Graphs" part
  * of section 4 of the neuralmasteryai page "Hardware Acceleration & Custom

@@ -256,3 +256,64 @@ def test_rmsnorm_binding_value_errors():
         hfa.rmsnorm(x, torch.ones(15))
     with pytest.raises(ValueError):
         hfa.rmsnorm(x.double(), w.double())
+
+
+# ---- key split entry point ---------------------------------------------------
+
+WS = 0x10000000
+
+
+def _split_call(splits=4, workspace=WS, workspace_bytes=1 << 30, **kw):
+    a = dict(GOOD, B=1, H=2, N=1000, d=128, scale=0.125, dtype=hfa.HFA_BF16, stream=None)
+    a.update(kw)
+    return hfa.hfa_attn_fwd_split(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                                  a["scale"], a["dtype"], splits, workspace, workspace_bytes, a["stream"])
+
+
+def test_split_plan_and_workspace_size():
+    # B*H*ceil(N/256) row tiles below 256 split their keys (bf16 only); the
+    # workspace holds [splits][B*H][N][d] + [splits][B*H][N] fp32.
+    # as many ranges as fit one round of 256 workgroups, each >= 32 key tiles
+    assert hfa.hfa_key_splits(hfa.HFA_BF16, 1, 8, 4096, 128) == 2
+    assert hfa.hfa_key_splits(hfa.HFA_BF16, 1, 2, 16384, 128) == 2
+    assert hfa.hfa_key_splits(hfa.HFA_BF16, 1, 1, 16384, 128) == 4
+    assert hfa.hfa_key_splits(hfa.HFA_BF16, 1, 1, 32768, 64) == 2
+    assert hfa.hfa_key_splits(hfa.HFA_BF16, 1, 1, 65536, 64) == 1    # 256 row tiles
+    assert hfa.hfa_key_splits(hfa.HFA_BF16, 1, 16, 1024, 128) == 1    # ranges would be too short
+    assert hfa.hfa_key_splits(hfa.HFA_BF16, 1, 16, 16384, 128) == 1   # 1024 workgroups already
+    assert hfa.hfa_key_splits(hfa.HFA_BF16, 2, 32, 4096, 128) == 1
+    assert hfa.hfa_key_splits(hfa.HFA_F32, 1, 8, 4096, 64) == 1
+    assert hfa.hfa_key_splits(hfa.HFA_BF16, 1, 1, 64, 128) == 1       # one key tile: nothing to split
+    assert hfa.hfa_key_splits(hfa.HFA_BF16, 0, 1, 64, 128) == 0
+    assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_BF16, 1, 8, 4096, 128, 0) == 2 * 8 * 4096 * 129 * 4
+    assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_BF16, 1, 16, 1024, 128, 0) == 0
+    assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_BF16, 1, 16, 1024, 128, 4) == 4 * 16 * 1024 * 129 * 4
+    assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_BF16, 1, 16, 1024, 128, 1) == 0
+    # 16 key tiles asked to split 5 ways: ranges of 4 tiles, so 4 ranges
+    assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_BF16, 1, 1, 1024, 64, 5) == 4 * 1024 * 65 * 4
+    # more ranges than key tiles: one range per tile
+    assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_BF16, 1, 1, 200, 64, 32) == 4 * 200 * 65 * 4
+    assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_F32, 1, 1, 1000, 64, 2) == -1
+    assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_BF16, 1, 1, 1000, 64, -1) == -1
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(splits=-1), hfa.HFA_ERR_SHAPE),
+    (dict(dtype=hfa.HFA_F32, d=64, splits=2), hfa.HFA_ERR_UNSUPPORTED),
+    (dict(workspace=None), hfa.HFA_ERR_NULL),
+    (dict(workspace=WS + 8), hfa.HFA_ERR_ALIGN),
+    (dict(workspace_bytes=4 * 2 * 1000 * 129 * 4 - 1), hfa.HFA_ERR_WORKSPACE),
+    (dict(workspace=GOOD["q"] - 4096), hfa.HFA_ERR_ALIAS),     # overlaps q
+    (dict(workspace=GOOD["lse"]), hfa.HFA_ERR_ALIAS),          # overlaps lse
+    (dict(N=0), hfa.HFA_ERR_SHAPE),
+    (dict(o=None), hfa.HFA_ERR_NULL),
+])
+def test_split_validation_rejects_before_any_device_call(kw, status):
+    assert _split_call(**kw) == status
+
+
+def test_split_one_needs_no_workspace():
+    if torch.cuda.is_available():
+        pytest.skip("would launch on a visible GPU with fake pointers")
+    assert _split_call(splits=1, workspace=None, workspace_bytes=0) == hfa.HFA_ERR_NO_DEVICE
+    assert _split_call(splits=4, workspace_bytes=4 * 2 * 1000 * 129 * 4) == hfa.HFA_ERR_NO_DEVICE

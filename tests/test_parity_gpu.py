@@ -342,3 +342,61 @@ def test_addresses_with_bit31_set(dtype, d, N):
     assert_close(f"bit31 {dtype} N={N} d={d}", od.float().cpu().double().numpy(), ld.cpu().double().numpy(),
                  ro, rl, dtype)
     del pool, pool2
+
+
+# ---- key split (hfa_attn_fwd_split) -----------------------------------------
+
+def run_gpu_split(q, k, v, scale, splits):
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev) for t in (q, k, v))
+    o, lse = hfa.attn_fwd(qd, kd, vd, scale, splits=splits)
+    torch.cuda.synchronize()
+    return o.float().cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("B,H,N,splits", [(1, 2, 1000, 0), (1, 2, 1000, 2), (1, 3, 777, 3), (2, 1, 4097, 7),
+                                          (1, 16, 1024, 0), (1, 1, 65, 2), (1, 1, 300, 32), (1, 4, 2048, 5)])
+def test_bf16_key_split(d, B, H, N, splits):
+    # Ranges of whole 64-key tiles, the last one ragged where N is; 0 = the
+    # library's choice.  Checked on every row against the oracle.
+    q, k, v = W.make_inputs(B, H, N, d, "bf16", seed=8000 + N + d + splits)
+    name = f"bf16 split={splits} (auto {hfa.hfa_key_splits(hfa.HFA_BF16, B, H, N, d)}) B={B} H={H} N={N} d={d}"
+    _log(f"[parity] {name}")
+    go, gl = run_gpu_split(q, k, v, 1.0 / math.sqrt(d), splits)
+    ro, rl = run_oracle(q, k, v, 1.0 / math.sqrt(d))
+    assert_close(name, go, gl, ro, rl, "bf16")
+
+
+def test_bf16_key_split_rising_scores():
+    # The running max moves on most tiles (see test_rising_scores), and each key
+    # range starts from its own first tile: the merge must rescale ranges whose
+    # maxima differ by tens of log2 units.
+    N, d = 1000, 128
+    g = torch.Generator("cpu").manual_seed(902)
+    e = torch.ones(d) / math.sqrt(d)
+    slope = torch.linspace(-0.2, 1.0, N).view(N, 1)
+    ramp = torch.linspace(0.0, 1.0, N).view(N, 1)
+    q = (torch.randn(1, 2, N, d, generator=g) + 8.0 * slope * e).to(torch.bfloat16).contiguous()
+    k = (torch.randn(1, 2, N, d, generator=g) + 20.75 * math.sqrt(d) * ramp * e).to(torch.bfloat16).contiguous()
+    v = torch.randn(1, 2, N, d, generator=g).to(torch.bfloat16).contiguous()
+    go, gl = run_gpu_split(q, k, v, 1.0 / math.sqrt(d), 4)
+    ro, rl = run_oracle(q, k, v, 1.0 / math.sqrt(d))
+    assert_close("bf16 split=4 rising", go, gl, ro, rl, "bf16")
+
+
+def test_split_with_caller_workspace_and_repeat():
+    # A caller workspace (leftover contents from an earlier call of another
+    # shape) and two calls in a row give the same bits.
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in W.make_inputs(1, 4, 1500, 128, "bf16", seed=8100))
+    need = hfa.hfa_attn_fwd_workspace_size(hfa.HFA_BF16, 1, 4, 1500, 128, 6)
+    ws = torch.full((need + 4096,), 0x7f, dtype=torch.uint8, device=dev)
+    o1, l1 = hfa.attn_fwd(q, k, v, splits=6, workspace=ws)
+    o2, l2 = hfa.attn_fwd(q, k, v, splits=6, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    o3, l3 = hfa.attn_fwd(q, k, v, splits=1)
+    torch.cuda.synchronize()
+    assert (o1.float() - o3.float()).abs().max().item() <= 2e-2
+    assert (l1 - l3).abs().max().item() <= 1e-3
