@@ -35,7 +35,7 @@ HFA_ERR_EPS = 9
 HFA_ERR_WORKSPACE = 10
 
 EXPORTED = ("hfa_attn_fwd", "hfa_status_str", "hfa_block_rows", "hfa_key_splits", "hfa_attn_fwd_workspace_size",
-            "hfa_attn_fwd_split", "hfa_attn_fwd_graph_create", "hfa_graph_launch", "hfa_graph_destroy",
+            "hfa_attn_fwd_split", "hfa_attn_fwd_split_noalloc", "hfa_attn_fwd_graph_create", "hfa_graph_launch", "hfa_graph_destroy",
             "hfa_softmax_rows", "hfa_rmsnorm")
 
 _lib = None
@@ -76,6 +76,9 @@ def load_library(path: str | Path | None = None) -> ctypes.CDLL:
     lib.hfa_attn_fwd_split.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int, i64, vp,
                                        i64, vp]
     lib.hfa_attn_fwd_split.restype = ctypes.c_int
+    lib.hfa_attn_fwd_split_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
+                                               i64, vp]
+    lib.hfa_attn_fwd_split_noalloc.restype = ctypes.c_int
     lib.hfa_attn_fwd_graph_create.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_float, ctypes.c_int,
                                               i64, ctypes.POINTER(vp)]
     lib.hfa_attn_fwd_graph_create.restype = ctypes.c_int
@@ -117,6 +120,11 @@ def hfa_attn_fwd_split(q, k, v, o, lse, B, H, N, d, scale, dtype, splits, worksp
     """Raw C-ABI call: pointers as ints (device addresses) or None; returns the status."""
     return load_library().hfa_attn_fwd_split(q, k, v, o, lse, B, H, N, d, scale, dtype, splits, workspace,
                                              workspace_bytes, stream)
+
+
+def hfa_attn_fwd_split_noalloc(q, k, v, o, lse, B, H, N, d, scale, dtype, splits, stream) -> int:
+    """Raw C-ABI call (the library's own scratch as workspace): pointers as ints; returns the status."""
+    return load_library().hfa_attn_fwd_split_noalloc(q, k, v, o, lse, B, H, N, d, scale, dtype, splits, stream)
 
 
 def hfa_attn_fwd_graph_create(q, k, v, o, lse, B, H, N, d, scale, dtype, count):

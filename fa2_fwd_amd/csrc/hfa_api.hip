@@ -14,6 +14,11 @@
 #include "attn_f32.hpp"
 #include "api_util.hpp"
 
+// Scratch of the allocation-free key split (hfa_attn_fwd_split_noalloc): 64 MiB,
+// one copy per GPU the library runs on, held until the process ends.
+constexpr int64_t kScratchBytes = int64_t{64} << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
 namespace {
 
 using namespace hfa;
@@ -231,6 +236,31 @@ hfa_status dispatch(const void* q, const void* k, const void* v, void* o, float*
   return launch_f32<F32D128>(q, k, v, o, lse, BH, N, scale, st, launch);
 }
 
+// ---- allocation-free key split ----------------------------------------------
+// The workspace of hfa_attn_fwd_split_noalloc: a file-scope device array, one
+// copy per GPU the library runs on, held until the process ends.  Host code
+// never passes the array's name to a kernel (on the host it is a stand-in, not
+// a device address): it takes each device's address once with
+// hipGetSymbolAddress, that device current, and passes that.
+
+// This device's address of `scratch` (nullptr if it cannot be had).
+void* scratch_address(int dev) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  if (dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
 }  // namespace
 
 // A captured and instantiated sequence of attention launches.
@@ -321,6 +351,33 @@ hfa_status hfa_attn_fwd_split(const void* q, const void* k, const void* v, void*
   const hfa_status dev = check_device();
   if (dev != HFA_OK) return dev;
   return dispatch(q, k, v, o, lse, BH, N, d, scale, dtype, static_cast<hipStream_t>(stream), true, ks, workspace);
+}
+
+hfa_status hfa_attn_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                      int64_t B, int64_t H, int64_t N, int64_t d, float scale, hfa_dtype dtype,
+                                      int64_t splits, void* stream) {
+  const hfa_status st = validate(q, k, v, o, lse, B, H, N, d, scale, dtype);
+  if (st != HFA_OK) return st;
+  if (splits < 0) return HFA_ERR_SHAPE;
+  const int64_t BH = B * H;
+  if (BH > INT_MAX / N) return HFA_ERR_SHAPE;
+  if (splits == 0) splits = auto_splits(dtype, BH, N, d);
+  if (dtype != HFA_BF16 && splits > 1) return HFA_ERR_UNSUPPORTED;
+  const KeySplit ks = make_split(N, splits);
+  if (split_workspace_bytes(ks.nsplit, BH, N, d) > kScratchBytes) return HFA_ERR_WORKSPACE;
+  const hfa_status devst = check_device();
+  if (devst != HFA_OK) return devst;
+  void* work = nullptr;
+  if (ks.nsplit > 1) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return HFA_ERR_NO_DEVICE;
+    }
+    work = scratch_address(dev);
+    if (!work) return HFA_ERR_LAUNCH;
+  }
+  return dispatch(q, k, v, o, lse, BH, N, d, scale, dtype, static_cast<hipStream_t>(stream), true, ks, work);
 }
 
 hfa_status hfa_attn_fwd_graph_create(const void* q, const void* k, const void* v, void* o, float* lse,

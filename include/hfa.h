@@ -154,6 +154,21 @@ hfa_status hfa_attn_fwd_split(const void* q, const void* k, const void* v, void*
                               int64_t B, int64_t H, int64_t N, int64_t d, float scale, hfa_dtype dtype,
                               int64_t splits, void* workspace, int64_t workspace_bytes, void* stream);
 
+/* hfa_attn_fwd_split for callers that cannot allocate device memory: code
+ * under stream or graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments and results as hfa_attn_fwd_split without the
+ * workspace: the partial results go to a scratch array inside the library, of
+ * 64 MiB, one per GPU (allocated when the library is loaded on that GPU and
+ * held until the process ends); the call itself allocates nothing.  A split
+ * whose workspace (hfa_attn_fwd_workspace_size) exceeds 64 MiB is rejected
+ * with HFA_ERR_WORKSPACE before any HIP call.  Every call on one GPU shares
+ * that GPU's array: calls that overlap in time on one GPU (other streams,
+ * other threads) race and must be serialised by the caller.  The array needs
+ * no clearing; the last call's partial results stay in it. */
+hfa_status hfa_attn_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                      int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                                      hfa_dtype dtype, int64_t splits, void* stream);
+
 /* Graph replay for launch-bound shapes.  Following the "CUDA Graphs" part
  * of section 4 of the neuralmasteryai page "Hardware Acceleration & Custom
  * Kernels" (per-kernel CPU dispatch costs microseconds; a graph captured once

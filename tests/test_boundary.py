@@ -317,3 +317,15 @@ def test_split_one_needs_no_workspace():
         pytest.skip("would launch on a visible GPU with fake pointers")
     assert _split_call(splits=1, workspace=None, workspace_bytes=0) == hfa.HFA_ERR_NO_DEVICE
     assert _split_call(splits=4, workspace_bytes=4 * 2 * 1000 * 129 * 4) == hfa.HFA_ERR_NO_DEVICE
+
+
+def test_noalloc_rejects_before_any_device_call():
+    # validation and the 64 MiB scratch limit come before any HIP call
+    a = dict(GOOD, B=1, H=64, N=4096, d=128)
+    call = lambda splits, **kw: hfa.hfa_attn_fwd_split_noalloc(  # noqa: E731
+        kw.get("q", a["q"]), a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], 0.125,
+        kw.get("dtype", hfa.HFA_BF16), splits, None)
+    assert call(8) == hfa.HFA_ERR_WORKSPACE            # 8 x 64 x 4096 x 129 x 4 bytes > 64 MiB
+    assert call(-1) == hfa.HFA_ERR_SHAPE
+    assert call(2, dtype=hfa.HFA_F32) == hfa.HFA_ERR_UNSUPPORTED
+    assert call(2, q=None) == hfa.HFA_ERR_NULL
