@@ -321,7 +321,9 @@ def test_split_one_needs_no_workspace():
 
 def test_noalloc_rejects_before_any_device_call():
     # validation and the 64 MiB scratch limit come before any HIP call
-    a = dict(GOOD, B=1, H=64, N=4096, d=128)
+    # fake addresses far enough apart for 64 MiB tensors
+    a = dict(q=0x10_0000_0000, k=0x20_0000_0000, v=0x30_0000_0000, o=0x40_0000_0000, lse=0x50_0000_0000,
+             B=1, H=64, N=4096, d=128)
     call = lambda splits, **kw: hfa.hfa_attn_fwd_split_noalloc(  # noqa: E731
         kw.get("q", a["q"]), a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], 0.125,
         kw.get("dtype", hfa.HFA_BF16), splits, None)
