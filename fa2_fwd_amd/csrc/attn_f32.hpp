@@ -76,7 +76,7 @@ struct F32Tile {
   static constexpr int BR = WQ * NW;  // queries per workgroup
   static constexpr int NT = 64 * NW;
   static constexpr int NSL = 5;           // int8 slices per fp32 value
-  static constexpr int KSROW = D + 16;    // bytes per key row of one slice plane (padded: 16 rows, 16 bank groups)
+  static constexpr int KSROW = D == 64 ? 96 : D;  // bytes per key row of one slice plane (see kswz)
   static constexpr int KSPLANEB = KT * KSROW;
   static constexpr int KEXPB = NSL * KSPLANEB;  // offset of the per-key exponents (int32)
   static constexpr int KTILEB = KEXPB + KT * 4;  // the slice planes, then each key's exponent
@@ -93,6 +93,31 @@ struct F32Tile {
   static_assert(CH == 16 || CH == 32, "a K row spans 16 or 32 lanes (d = 64 or 128)");
   static_assert(VITEMS >= 1 && ((KT / 32) * 4 * D) % NT == 0, "V items must divide evenly over the threads");
 };
+
+// K slice planes, laid out for conflict-free LDS access on gfx950 (measured
+// with SQ_LDS_BANK_CONFLICT on probe patterns):
+//  * The score reads take 16 bytes per lane: chunk g (+ 4h) of 16 consecutive
+//    rows, the four lane groups g side by side.  With rows at an odd multiple
+//    of 32 bytes apart these are conflict-free; with rows 64 or 80 bytes apart
+//    (any XOR of the chunk tried) they cost 4 extra cycles per read.  So d = 64
+//    rows are 96 bytes apart (32 bytes of padding).  At d = 128, rows 128
+//    bytes apart with chunk c stored at chunk c ^ ((r / 2) % 8) are
+//    conflict-free.
+//  * The staging stores take 4 bytes per lane, 4 rows of 64 bytes (d = 64) or
+//    2 of 128 bytes (d = 128) per wave instruction; they are conflict-free when
+//    those rows cover disjoint 64-dword bank windows.  96-byte rows start 24
+//    dwords apart, so a wave stores rows of one parity within a group of 8
+//    (stage_row): windows at 0, 48, 32, 16 or 24, 8, 56, 40.
+template <int D>
+__device__ __forceinline__ int kswz(int row) {
+  return D == 64 ? 0 : (row >> 1) & 7;
+}
+// The key row (within a tile) that staging position q (= thread index / CH,
+// per load) takes: at d = 64, positions 8k + m go to rows 8k + 2 (m % 4) + m / 4.
+template <int D>
+__device__ __forceinline__ int stage_row(int q) {
+  return D == 64 ? (q & ~7) | ((q & 3) << 1) | ((q >> 2) & 1) : q;
+}
 
 // The values of x in the lane pair (l, l ^ 16) or (l, l ^ 32), in an order that
 // depends on the lane (use in symmetric operations only).  gfx950's
@@ -398,7 +423,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
 #pragma unroll
     for (int u = 0; u < T::LOADS; ++u) {
       const int idx = tid_here + u * T::NT;
-      const int row = idx / T::CH, ch = idx % T::CH;
+      const int row = stage_row<D>(idx / T::CH), ch = idx % T::CH;
       const int key = j * KT + row;
       u32x4 kx = {0u, 0u, 0u, 0u};
       if (full || key < N) kx = *reinterpret_cast<const u32x4*>(Kh + static_cast<size_t>(key) * D + ch * 4);
@@ -425,7 +450,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
 #pragma unroll
     for (int u = 0; u < T::LOADS; ++u) {
       const int idx = tid + u * T::NT;
-      const int row = idx / T::CH, ch = idx % T::CH;
+      const int row = stage_row<D>(idx / T::CH), ch = idx % T::CH;
       const f32x4 x = __builtin_bit_cast(f32x4, kreg[u]);
       float mx = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
       // this lane's part of the row's L1 norm (its column chunk is the same in
@@ -438,11 +463,17 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
       slice5(x, e, w);
       // One opaque address for this lane's five slice stores (the planes are
       // immediate offsets from it), recomputed here like the thread index.
-      int off0 = row * T::KSROW + 4 * ch;
+      int off0 = row * T::KSROW + (((ch >> 2) ^ kswz<D>(row)) << 4) + 4 * (ch & 3);
       asm volatile("" : "+v"(off0));
 #pragma unroll
       for (int a2 = 0; a2 < T::NSL; ++a2) *reinterpret_cast<uint32_t*>(kt + off0 + a2 * T::KSPLANEB) = w[a2];
-      if (ch == 0) *reinterpret_cast<int*>(kt + T::KEXPB + 4 * row) = e;
+      if (ch == 0) {
+        // the row again from an opaque thread index: its address is not kept
+        // (or spilled) across the key loop
+        int tid_e = tid;
+        asm volatile("" : "+v"(tid_e));
+        *reinterpret_cast<int*>(kt + T::KEXPB + 4 * stage_row<D>((tid_e + u * T::NT) / T::CH)) = e;
+      }
       kmax_e = max(kmax_e, e);
     }
     // Split each V value into three bf16 pieces by truncation: x1 keeps the
@@ -533,7 +564,8 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
       for (int h = 0; h < D / 64; ++h)
 #pragma unroll
         for (int a2 = 0; a2 < T::NSL; ++a2)
-          ks[h][a2] = __builtin_bit_cast(i32x4, lds_load16(kt, a2 * T::KSPLANEB + (kb * 16 + i16) * T::KSROW + 64 * h + 16 * g));
+          ks[h][a2] = __builtin_bit_cast(
+              i32x4, lds_load16(kt, a2 * T::KSPLANEB + (kb * 16 + i16) * T::KSROW + (((4 * h + g) ^ kswz<D>(i16)) << 4)));
       const i32x4 ek = __builtin_bit_cast(i32x4, lds_load16(kt, T::KEXPB + (kb * 16 + 4 * g) * 4));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
