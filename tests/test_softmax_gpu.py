@@ -94,3 +94,47 @@ def test_softmax_rows_rows_sum_to_one_on_device():
     y = hfa.softmax_rows(x.cuda())
     s = y.double().sum(dim=1)
     assert torch.all((s - 1).abs() < 1e-4)
+
+
+# Rows wider than the register-resident limit (32768 columns) with 16-byte
+# accesses: the streaming kernel, at widths around chunk boundaries and far past them.
+WIDE = [(3, 32772), (2, 72700), (2, 72704), (2, 90000), (2, 105472), (2, 138236), (2, 138240), (2, 156668),
+        (2, 156672), (2, 156676), (2, 300000), (1, 1 << 20)]
+
+
+@pytest.mark.parametrize("rows,cols", WIDE)
+def test_softmax_rows_wide(rows, cols):
+    x = _x(rows, cols, seed=rows + cols)
+    y = hfa.softmax_rows(x.cuda())
+    torch.cuda.synchronize()
+    _check(f"wide {rows}x{cols}", x, y)
+
+
+@pytest.mark.parametrize("cols", [100000, 262144])
+def test_softmax_rows_wide_in_place(cols):
+    # every element is read (twice) by the thread that writes it, before it writes it
+    x = _x(3, cols, seed=cols + 1)
+    xd = x.cuda()
+    y = hfa.softmax_rows(xd, out=xd)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == xd.data_ptr()
+    _check(f"wide in place 3x{cols}", x, xd)
+
+
+def test_softmax_rows_wide_large_magnitudes_and_minus_inf():
+    # peaked and shifted rows (the running max moves from chunk to chunk), runs
+    # of -inf entries, the largest value in the last column
+    x = _x(2, 200000, seed=11, scale=30.0, shift=-500.0)
+    x[:, 156000:157000] = -float("inf")
+    x[:, :5] = -float("inf")
+    x[0, 199999] = 400.0
+    y = hfa.softmax_rows(x.cuda()).cpu().double().numpy()
+    keep = ~torch.isinf(x)
+    ref = np.zeros(tuple(x.shape))
+    for r in range(2):
+        cols = keep[r].numpy()
+        ref[r, cols] = oracle.softmax_rows(x[r:r + 1, cols].contiguous().numpy())[0]
+    assert np.all(y[~keep.numpy()] == 0.0)
+    err = np.abs(y - ref).max()
+    print(f"[softmax] wide peaked/-inf: max|d|={err:.3e}", flush=True)
+    assert err <= ATOL
