@@ -166,10 +166,15 @@ __device__ __forceinline__ void dma16(const char* base, int voff, char* lds) {
   const uint32_t b_hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b >> 32))));
   const uint64_t sbase = (static_cast<uint64_t>(b_hi) << 32) | static_cast<uint64_t>(b_lo);
   // M0 carries the LDS destination; its previous value is restored, so the
-  // statement leaves every register the compiler may rely on unchanged.
+  // statement leaves every register the compiler may rely on unchanged.  A
+  // scalar write of M0 needs one wait state before a load to LDS reads it;
+  // the compiler cannot see into the statement, so the s_nop is written here.
+  // (The scalar operands come from readfirstlane, and a VALU write of an SGPR
+  // needs five wait states before a vector-memory read of it; the compiler
+  // hoists them out of the key loop, far from any use.)
   uint32_t saved_m0;
   asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
       : "=&s"(saved_m0)
       : "s"(lds_addr), "v"(voff), "s"(sbase)
       : "memory");
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   char* const kbuf = smem;                    // K ring: NBUF tile buffers
   char* const vbuf = smem + T::NBUF * TILEB;  // V ring: NBUF tile buffers
 
-  const int tid = threadIdx.x;
+  const int tid = thread_id();
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in scalar registers
   const int grp = wave >> 2;  // ping-pong group; waves w and w + 4 share a SIMD
@@ -219,7 +224,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   // Logical tile order: q-tile fastest, then the key range, then the head,
   // so that the workgroups sharing a head's key range are neighbours (and,
   // after xcd_remap, on one XCD).
-  const int tile = xcd_remap(blockIdx.x, total_wg);
+  const int tile = xcd_remap(group_id(), total_wg);
   const int grp_id = tile / n_qt, qt = tile - grp_id * n_qt;
   const int sp = SPLIT ? grp_id % sa.nsplit : 0;
   const int bh = SPLIT ? grp_id / sa.nsplit : grp_id;
@@ -753,8 +758,8 @@ __global__ __launch_bounds__(256) void attn_merge_bf16_kernel(const float* __res
                                                               __bf16* __restrict__ O, float* __restrict__ LSE,
                                                               int rows, int nsplit) {
   constexpr int TPR = D / 8;  // threads per row
-  const int row = blockIdx.x * (256 / TPR) + static_cast<int>(threadIdx.x) / TPR;
-  const int c0 = (static_cast<int>(threadIdx.x) % TPR) * 8;
+  const int row = group_id() * (256 / TPR) + thread_id() / TPR;
+  const int c0 = (thread_id() % TPR) * 8;
   if (row >= rows) return;
   float m = -INFINITY;
   for (int s = 0; s < nsplit; ++s) m = fmaxf(m, part_lse[static_cast<size_t>(s) * rows + row]);

@@ -238,9 +238,8 @@ template <int D, int QB>
 __device__ __forceinline__ void exact_rows_impl(const float* __restrict__ Qh, const float* __restrict__ Kh,
                                                          const float* __restrict__ Vh, float* __restrict__ Oh,
                                                          float* __restrict__ lse_h, int N, int qrow0, double c2,
-                                                         float qmul) {
+                                                         float qmul, int lane) {
   constexpr int DQ = D / 4;
-  const int lane = threadIdx.x & 63;
   const int i16 = lane & 15, g = lane >> 4;
   const int pi = 4 * (i16 & 3) + (i16 >> 2);  // key of A row i16 within a 16-key block
   f64x4 acc[QB][D / 16];
@@ -256,14 +255,14 @@ __device__ __forceinline__ void exact_rows_impl(const float* __restrict__ Qh, co
     f64x4 s[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) s[qb] = f64x4{0.0, 0.0, 0.0, 0.0};
-    const float* krow = Kh + static_cast<size_t>(min(k0 + pi, N - 1)) * D + g * DQ;
+    const float* krow = Kh + (min(k0 + pi, N - 1) * D + g * DQ);
 #pragma unroll 2
     for (int t4 = 0; t4 < DQ / 4; ++t4) {
       const f32x4 kf = *reinterpret_cast<const f32x4*>(krow + 4 * t4);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int row = min(qrow0 + 16 * qb + i16, N - 1);
-        const f32x4 qf = *reinterpret_cast<const f32x4*>(Qh + static_cast<size_t>(row) * D + g * DQ + 4 * t4) * qmul;
+        const f32x4 qf = *reinterpret_cast<const f32x4*>(Qh + (row * D + g * DQ + 4 * t4)) * qmul;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           s[qb] = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(kf[e]), static_cast<double>(qf[e]), s[qb],
@@ -294,7 +293,7 @@ __device__ __forceinline__ void exact_rows_impl(const float* __restrict__ Qh, co
         f64x4 a = acc[qb][n] * alpha;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const float vv = Vh[static_cast<size_t>(min(k0 + 4 * g + t, N - 1)) * D + 16 * n + i16];
+          const float vv = Vh[min(k0 + 4 * g + t, N - 1) * D + 16 * n + i16];
           a = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(vv), p[t], a, 0, 0, 0);
         }
         acc[qb][n] = a;
@@ -306,7 +305,7 @@ __device__ __forceinline__ void exact_rows_impl(const float* __restrict__ Qh, co
     const double l_tot = add_xor<32>(add_xor<16>(l_run[qb]));
     const int row = qrow0 + 16 * qb + i16;
     if (row < N) {
-      float* orow = Oh + static_cast<size_t>(row) * D;
+      float* orow = Oh + row * D;
 #pragma unroll
       for (int n = 0; n < D / 16; ++n)
 #pragma unroll
@@ -324,7 +323,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
   constexpr int D = T::D, QB = T::QB, KT = T::KT;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
-  const int tid = threadIdx.x;
+  const int tid = thread_id();
   const int lane = tid & 63, wave = tid >> 6;
   const int i16 = lane & 15, g = lane >> 4;
   // With 8 waves, waves 4..7 (one per SIMD) take the tile's phases in another
@@ -335,9 +334,16 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
   constexpr bool kSkew = HFA_F32_SKEW && T::NW == 8;
   const bool late = kSkew && __builtin_amdgcn_readfirstlane(tid >> 6) >= T::NW / 2;
 
-  const int tile = xcd_remap(blockIdx.x, total_wg);
-  const int bh = tile / n_qt, qt = tile - bh * n_qt;
+  // Workgroup-uniform indices, kept in scalar registers (the division runs on
+  // the vector unit; left there, every per-head pointer below would occupy
+  // vector registers for the whole kernel).
+  const int tile = xcd_remap(group_id(), total_wg);
+  const int bh = uniform_sgpr(tile / n_qt);
+  const int qt = uniform_sgpr(tile - bh * n_qt);
+  // Per-head pointers (wave-uniform); offsets within a head fit in 32 bits
+  // (N d < 2^31), so per-lane row offsets stay 32-bit.
   const size_t head = static_cast<size_t>(bh) * static_cast<size_t>(N) * D;
+  float* const lse_h = LSE + static_cast<size_t>(bh) * N;
   const float* Qh = Q + head;
   const float* Kh = K + head;
   const float* Vh = V + head;
@@ -364,7 +370,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) {
         f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (row < N) v = *reinterpret_cast<const f32x4*>(Qh + static_cast<size_t>(row) * D + 64 * h + 16 * g + 4 * t4);
+        if (row < N) v = *reinterpret_cast<const f32x4*>(Qh + (row * D + 64 * h + 16 * g + 4 * t4));
         v *= qmul;
         x[h][t4] = v;
         mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
@@ -426,7 +432,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
       const int row = stage_row<D>(idx / T::CH), ch = idx % T::CH;
       const int key = j * KT + row;
       u32x4 kx = {0u, 0u, 0u, 0u};
-      if (full || key < N) kx = *reinterpret_cast<const u32x4*>(Kh + static_cast<size_t>(key) * D + ch * 4);
+      if (full || key < N) kx = *reinterpret_cast<const u32x4*>(Kh + (key * D + ch * 4));
       kreg[u] = kx;
     }
 #pragma unroll
@@ -437,7 +443,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int key = j * KT + 32 * c + 16 * (i >> 2) + 4 * g8 + (i & 3);
-        vreg[it][i] = (full || key < N) ? Vh[static_cast<size_t>(key) * D + vcol] : 0.0f;
+        vreg[it][i] = (full || key < N) ? Vh[key * D + vcol] : 0.0f;
       }
     }
   };
@@ -703,6 +709,15 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
   for (; j < ntiles; ++j) tile_step(j, 0, std::false_type{});
 
 
+  // The lane and the wave's first query row, recomputed after the key loop
+  // from an opaque copy of the thread index: nothing the epilogue needs is
+  // kept (or spilled) across the loop.
+  int tid_after = tid;
+  asm volatile("" : "+v"(tid_after));
+  const int lane_after = tid_after & 63;
+  const int wave_after = uniform_sgpr(tid_after >> 6);
+  const int qrow0_after = qt * T::BR + wave_after * T::WQ;
+
   // ---- exactness check.  The workgroup's largest key exponent, and a bound
   // on its largest key L1 norm (the sum over the column chunks of each
   // chunk's largest L1 norm, over every row staged by any thread), go through
@@ -723,8 +738,8 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
       if (m >= T::CH) kmax_a = fmaxf(kmax_a, __shfl_xor(kmax_a, m));
     }
     int* kst = reinterpret_cast<int*>(smem + T::MISCB);
-    if (lane < T::CH) kst[wave * T::CH + lane] = __float_as_int(kmax_a);
-    if (lane == 0) kst[T::NW * T::CH + wave] = kmax_e;
+    if (lane_after < T::CH) kst[wave_after * T::CH + lane_after] = __float_as_int(kmax_a);
+    if (lane_after == 0) kst[T::NW * T::CH + wave_after] = kmax_e;
     lds_barrier_f32();
     float ak = 0.0f;
 #pragma unroll
@@ -743,7 +758,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
     const double bound = abs_scale * (__builtin_amdgcn_ldexp(bk * wave_a + bq * kmax_a, -35) +
                                       __builtin_amdgcn_ldexp(bq * bk, -40) * D);
     if (bound > kExactScoreBound) {
-      exact_rows_impl<D, QB>(Qh, Kh, Vh, Oh, LSE + static_cast<size_t>(bh) * N, N, qrow0, c2, qmul);
+      exact_rows_impl<D, QB>(Qh, Kh, Vh, Oh, lse_h, N, qrow0_after, c2, qmul, lane_after);
       return;
     }
   }
@@ -753,12 +768,12 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
   for (int qb = 0; qb < QB; ++qb) {
     const double l_tot = add_xor<32>(add_xor<16>(l_run[qb]));
     const float inv = static_cast<float>(1.0 / l_tot);
-    const int row = qrow0 + qb * 16 + i16;
+    const int row = qrow0_after + qb * 16 + (lane_after & 15);
     if (row < N) {
-      float* orow = Oh + static_cast<size_t>(row) * D;
+      float* orow = Oh + row * D + 4 * (lane_after >> 4);
 #pragma unroll
-      for (int n = 0; n < D / 16; ++n) *reinterpret_cast<f32x4*>(orow + 16 * n + 4 * g) = acc[qb][n] * inv;
-      if (g == 0) LSE[static_cast<size_t>(bh) * N + row] = static_cast<float>((m2[qb] + log2(l_tot)) * kLn2);
+      for (int n = 0; n < D / 16; ++n) *reinterpret_cast<f32x4*>(orow + 16 * n) = acc[qb][n] * inv;
+      if (lane_after < 16) lse_h[row] = static_cast<float>((m2[qb] + log2(l_tot)) * kLn2);
     }
   }
 }

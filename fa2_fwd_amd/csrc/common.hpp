@@ -19,6 +19,14 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr double kLn2 = 0.69314718055994530942;
 
+// Thread and workgroup indices read through the compiler builtins.  These
+// kernels are built without IEEE mode (-mno-amdgpu-ieee), and the runtime's
+// threadIdx/blockIdx helpers, built with it, are then not inlined: each read
+// becomes a call, and the workgroup index comes back in a vector register, so
+// the compiler no longer knows that it is uniform.
+__device__ __forceinline__ int thread_id() { return static_cast<int>(__builtin_amdgcn_workitem_id_x()); }
+__device__ __forceinline__ int group_id() { return static_cast<int>(__builtin_amdgcn_workgroup_id_x()); }
+
 // Workgroups are handed out round-robin over the 8 XCDs (wg % 8 selects the
 // XCD).  Remap the hardware id so that each XCD receives one contiguous range
 // of logical tiles: tiles of one (batch, head) then share that XCD's L2 for
@@ -28,6 +36,17 @@ __device__ __forceinline__ int xcd_remap(int wg, int total) {
   const int per = total / kXcd, rem = total % kXcd;
   const int xcd = wg % kXcd, local = wg / kXcd;
   return (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+// A wave-uniform int moved to a scalar register.  The empty asm makes the
+// value opaque, so the compiler cannot drop the readfirstlane by proving the
+// operand uniform (after which everything derived from it would stay in
+// vector registers); the readfirstlane itself is the compiler's, placed with
+// the wait state that gfx950 needs between a VALU write of the source and the
+// read (a hand-written one in inline asm would get none).
+__device__ __forceinline__ int uniform_sgpr(int x) {
+  asm volatile("" : "+v"(x));
+  return __builtin_amdgcn_readfirstlane(x);
 }
 
 // 2^x on the hardware exp unit (v_exp_f32); exp2(-inf) = 0.

@@ -75,8 +75,8 @@ __device__ __forceinline__ float group_sum(float v, float* lds) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
   if constexpr (G > 64) {
-    const int wave = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) lds[wave] = v;
+    const int wave = thread_id() >> 6;
+    if ((thread_id() & 63) == 0) lds[wave] = v;
     __syncthreads();
     const int first = (wave / (G / 64)) * (G / 64);
     v = lds[first];
@@ -93,8 +93,8 @@ __global__ __launch_bounds__(NT) void rmsnorm_kernel(const T* x, const T* res, c
   using E = RmsElt<T>;
   constexpr int PER = E::kPerSlot;
   __shared__ float lds[NT / 64];
-  const int t = threadIdx.x % G;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * (NT / G) + threadIdx.x / G;
+  const int t = thread_id() % G;
+  const int64_t row = static_cast<int64_t>(group_id()) * (NT / G) + thread_id() / G;
   const bool live = row < rows;
   const int64_t base = live ? row * cols : 0;
   const T* xr = x + base;

@@ -70,8 +70,8 @@ __device__ __forceinline__ SoftmaxPair merge_workgroup(SoftmaxPair p, SoftmaxPai
     const SoftmaxPair o = {__shfl_xor(p.m, off), __shfl_xor(p.l, off)};
     p = merge_pairs(p, o);
   }
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) lds[wave] = p;
+  const int wave = thread_id() >> 6;
+  if ((thread_id() & 63) == 0) lds[wave] = p;
   __syncthreads();
   SoftmaxPair t = lds[0];
 #pragma unroll
@@ -138,8 +138,8 @@ __device__ __forceinline__ void store_slots(float* yr, int64_t base, int64_t col
 template <int NT, int ITEMS, bool VEC>
 __global__ __launch_bounds__(NT) void softmax_rows_resident_kernel(const float* x, float* y, int64_t cols) {
   __shared__ SoftmaxPair lds[NT / 64];
-  const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
+  const int tid = thread_id();
+  const int64_t row = group_id();
   const float* xr = x + row * cols;
   float* yr = y + row * cols;
   float v[ITEMS * 4];
@@ -152,8 +152,8 @@ __global__ __launch_bounds__(NT) void softmax_rows_resident_kernel(const float* 
 template <int NT, int UNROLL, bool VEC>
 __global__ __launch_bounds__(NT) void softmax_rows_stream_kernel(const float* x, float* y, int64_t cols) {
   __shared__ SoftmaxPair lds[NT / 64];
-  const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
+  const int tid = thread_id();
+  const int64_t row = group_id();
   const float* xr = x + row * cols;
   float* yr = y + row * cols;
   constexpr int64_t STEP = static_cast<int64_t>(NT) * 4 * UNROLL;
