@@ -62,3 +62,55 @@ def test_noalloc_rejects_a_split_beyond_its_scratch():
     st = hfa.hfa_attn_fwd_split_noalloc(q.data_ptr(), q.data_ptr(), q.data_ptr(), o.data_ptr(), lse.data_ptr(),
                                         1, 64, 4096, 128, 0.125, hfa.HFA_BF16, 8, None)
     assert st == hfa.HFA_ERR_WORKSPACE
+
+
+def test_noalloc_replays_from_a_captured_graph():
+    """The callers this entry point is for capture it: a graph holding one call, replayed
+    three times with new inputs copied in eagerly between replays, each replay equal to
+    an eager hfa_attn_fwd_split call on the same inputs and within tolerance of the oracle."""
+    dev = torch.device("cuda:0")
+    B, H, N, d, splits = 1, 4, 2500, 128, 4
+    scale = 1.0 / math.sqrt(d)
+    inputs = [W.make_inputs(B, H, N, d, "bf16", seed=9100 + r) for r in range(3)]
+    q, k, v = (t.to(dev) for t in inputs[0])
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, N, device=dev)
+
+    def call(stream):
+        return hfa.hfa_attn_fwd_split_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                              lse.data_ptr(), B, H, N, d, scale, hfa.HFA_BF16, splits, stream)
+
+    # one eager call first: the library's per-device set-up happens outside the capture
+    assert call(torch.cuda.current_stream(dev).cuda_stream) == hfa.HFA_OK
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            assert call(torch.cuda.current_stream(dev).cuda_stream) == hfa.HFA_OK
+    torch.cuda.synchronize()
+
+    need = hfa.hfa_attn_fwd_workspace_size(hfa.HFA_BF16, B, H, N, d, splits)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    for r, (hq, hk, hv) in enumerate(inputs):
+        print(f"[noalloc graph] replay {r}: B={B} H={H} N={N} d={d} splits={splits}", flush=True)
+        q.copy_(hq.to(dev))
+        k.copy_(hk.to(dev))
+        v.copy_(hv.to(dev))
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o_ref = torch.empty_like(q)
+        l_ref = torch.empty_like(lse)
+        st = hfa.hfa_attn_fwd_split(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_ref.data_ptr(), l_ref.data_ptr(),
+                                    B, H, N, d, scale, hfa.HFA_BF16, splits, ws.data_ptr(), need,
+                                    torch.cuda.current_stream(dev).cuda_stream)
+        assert st == hfa.HFA_OK, hfa.hfa_status_str(st)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), f"replay {r}: O differs from the eager call"
+        assert torch.equal(lse, l_ref), f"replay {r}: LSE differs from the eager call"
+        ro, rl = run_oracle(hq, hk, hv, scale)
+        assert_close(f"noalloc graph replay {r}", o.float().cpu().double().numpy(), lse.cpu().double().numpy(),
+                     ro, rl, "bf16")
