@@ -59,12 +59,12 @@ namespace hfa {
 #define HFA_NBUF 4
 #endif
 
-template <int D_, int QB_, int NW_>
+template <int D_, int QB_, int NW_, int KT_ = 64>
 struct Bf16Tile {
   static constexpr int D = D_;        // head dim (64 or 128)
   static constexpr int QB = QB_;      // 32-query blocks per wave
   static constexpr int NW = NW_;      // waves per workgroup (two ping-pong groups)
-  static constexpr int KT = 64;       // keys per K/V tile
+  static constexpr int KT = KT_;      // keys per K/V tile (64 or 128)
   static constexpr int WQ = 32 * QB;  // queries per wave
   static constexpr int BR = WQ * NW;  // queries per workgroup (row-tile height)
   static constexpr int NT = 64 * NW;  // threads per workgroup

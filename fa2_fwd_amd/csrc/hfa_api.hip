@@ -99,11 +99,13 @@ struct KeySplit {
   int64_t nsplit;
   int64_t tiles;
 };
-constexpr int64_t kKeyTile = 64;   // keys per K/V tile of the bf16 kernel
 constexpr int64_t kMaxSplits = 32;
+// Keys per K/V tile of the bf16 kernel for head dim d: ranges are whole tiles.
+constexpr int64_t key_tile(int64_t d) { return d == 128 ? Bf16D128::KT : Bf16D64::KT; }
 
-KeySplit make_split(int64_t N, int64_t want) {
-  const int64_t ntiles = (N + kKeyTile - 1) / kKeyTile;
+KeySplit make_split(int64_t N, int64_t d, int64_t want) {
+  const int64_t kt = key_tile(d);
+  const int64_t ntiles = (N + kt - 1) / kt;
   const int64_t s = std::max<int64_t>(1, std::min<int64_t>({want, ntiles, kMaxSplits}));
   const int64_t tiles = (ntiles + s - 1) / s;
   return {(ntiles + tiles - 1) / tiles, tiles};
@@ -112,18 +114,17 @@ KeySplit make_split(int64_t N, int64_t want) {
 // The split hfa_attn_fwd_split chooses when asked for none in particular:
 // shapes whose 256-row tiles give fewer workgroups than compute units split
 // their keys into as many ranges as still fit one round of workgroups on the
-// compute units, each range at least kMinSplitTiles key tiles long (shorter
-// ranges lose more to the partial results' round trip through memory and the
+// compute units, each range at least kMinSplitKeys keys long (shorter ranges
+// lose more to the partial results' round trip through memory and the
 // per-workgroup start-up than they gain; measured on the device).
-constexpr int64_t kMinSplitTiles = 32;
+constexpr int64_t kMinSplitKeys = 2048;
 int64_t auto_splits(hfa_dtype dtype, int64_t BH, int64_t N, int64_t d) {
   if (dtype != HFA_BF16) return 1;
   const int64_t br = d == 128 ? Bf16D128::BR : Bf16D64::BR;
   const int64_t grid = BH * ((N + br - 1) / br);
   if (grid >= kComputeUnits) return 1;
-  const int64_t ntiles = (N + kKeyTile - 1) / kKeyTile;
-  const int64_t want = std::min<int64_t>(kComputeUnits / grid, ntiles / kMinSplitTiles);
-  return want < 2 ? 1 : make_split(N, want).nsplit;
+  const int64_t want = std::min<int64_t>(kComputeUnits / grid, N / kMinSplitKeys);
+  return want < 2 ? 1 : make_split(N, d, want).nsplit;
 }
 
 // Workspace bytes of a split launch: the partial outputs [nsplit][BH][N][d]
@@ -322,7 +323,7 @@ int64_t hfa_attn_fwd_workspace_size(hfa_dtype dtype, int64_t B, int64_t H, int64
   if (B * H > INT_MAX / N) return -1;
   if (splits == 0) splits = auto_splits(dtype, B * H, N, d);
   if (dtype != HFA_BF16 && splits > 1) return -1;
-  return split_workspace_bytes(make_split(N, splits).nsplit, B * H, N, d);
+  return split_workspace_bytes(make_split(N, d, splits).nsplit, B * H, N, d);
 }
 
 hfa_status hfa_attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
@@ -335,7 +336,7 @@ hfa_status hfa_attn_fwd_split(const void* q, const void* k, const void* v, void*
   if (BH > INT_MAX / N) return HFA_ERR_SHAPE;
   if (splits == 0) splits = auto_splits(dtype, BH, N, d);
   if (dtype != HFA_BF16 && splits > 1) return HFA_ERR_UNSUPPORTED;
-  const KeySplit ks = make_split(N, splits);
+  const KeySplit ks = make_split(N, d, splits);
   if (ks.nsplit > 1) {
     const int64_t need = split_workspace_bytes(ks.nsplit, BH, N, d);
     if (!workspace) return HFA_ERR_NULL;
@@ -363,7 +364,7 @@ hfa_status hfa_attn_fwd_split_noalloc(const void* q, const void* k, const void* 
   if (BH > INT_MAX / N) return HFA_ERR_SHAPE;
   if (splits == 0) splits = auto_splits(dtype, BH, N, d);
   if (dtype != HFA_BF16 && splits > 1) return HFA_ERR_UNSUPPORTED;
-  const KeySplit ks = make_split(N, splits);
+  const KeySplit ks = make_split(N, d, splits);
   if (split_workspace_bytes(ks.nsplit, BH, N, d) > kScratchBytes) return HFA_ERR_WORKSPACE;
   const hfa_status devst = check_device();
   if (devst != HFA_OK) return devst;
