@@ -81,6 +81,16 @@ def test_long_ragged_sequence(dtype, d):
     check_case(f"ragged {dtype} N={N} d={d}", q, k, v, 1.0 / math.sqrt(d), dtype, rows=rows)
 
 
+@pytest.mark.parametrize("B,H,N", [(1, 16, 4095), (1, 16, 4096), (1, 16, 5000), (2, 8, 8192), (1, 2, 8192)])
+def test_bf16_d64_long_key_tiles(B, H, N):
+    # bf16 d=64 calls that are not split take 128-key tiles from N = 4096 on (64-key tiles
+    # below, and in every split): both sides of the threshold, a ragged last tile, and a
+    # shape the automatic split takes (1x2x8192).
+    q, k, v = W.make_inputs(B, H, N, 64, "bf16", seed=6400 + N + H)
+    rows = W.sample_rows(N, 48, seed=N)
+    check_case(f"bf16 d=64 B={B} H={H} N={N}", q, k, v, 0.125, "bf16", rows=rows)
+
+
 @pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
 def test_very_long_sequence(dtype, d):
     # 2^18 + 1 keys: 4097 key tiles, one ragged; rows sampled across every query tile range.
