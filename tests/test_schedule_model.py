@@ -10,7 +10,10 @@ kernel relies on:
 1. every LDS read of a tile happens in an interval after the one whose
    closing barrier follows the requester's wait for that tile (group 0 waits
    for K_{j+1} at the end of its MFMA phase j, group 1 for V_j);
-2. a buffer is refilled only after every read of its previous tile is done.
+2. a buffer is refilled only after every read of its previous tile is done,
+   in an earlier interval: a group is four waves (one per SIMD) that are in
+   step only at barriers, so a refill requested in the same interval as a
+   read of the previous tile can overtake another wave's read.
 
 The per-phase lists mirror the kernel in fa2_fwd_amd/csrc/attn_bf16.hpp (a
 change there must be mirrored here); the ring depth NBUF is a build option
