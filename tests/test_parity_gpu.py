@@ -270,6 +270,18 @@ def test_bitwise_deterministic(dtype):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("B,H,N,d", [(4, 8, 2048, 64), (1, 8, 4096, 64), (1, 4, 4096, 128)])
+def test_f32_long_runs_bitwise_repeatable(B, H, N, d):
+    # the fp32 kernels' double-buffered LDS tiles, on every fp32 tiling
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in W.make_inputs(B, H, N, d, "f32", seed=78, qk_mult=4.0))
+    o0, l0 = hfa.attn_fwd(q, k, v)
+    for _ in range(2):
+        o, l = hfa.attn_fwd(q, k, v)
+        torch.cuda.synchronize()
+        assert torch.equal(o, o0) and torch.equal(l, l0)
+
+
 @pytest.mark.parametrize("B,H,N,d", [(1, 8, 4096, 128), (2, 16, 8192, 64), (2, 32, 4096, 128)])
 def test_bf16_long_runs_bitwise_repeatable(B, H, N, d):
     # Three runs of long bf16 sequences (64 key tiles and more; a grid of half the CUs, the
