@@ -173,3 +173,19 @@ def test_rmsnorm_benchmark_workloads(cfg):
     rng = np.random.default_rng(cfg)
     rows = np.unique(np.r_[0, wl.rows // 2, wl.rows - 1, rng.integers(0, wl.rows, 45)])
     _check(wl.describe(), x, r, w, wl.eps, y, None, rows=rows)
+
+
+@pytest.mark.parametrize("rows,cols,dtype", [(131072, 512, torch.float32), (8192, 8192, torch.float32),
+                                             (16384, 8192, torch.bfloat16)])
+def test_rmsnorm_bitwise_repeatable(rows, cols, dtype):
+    # three runs of the residual-add + RMSNorm kernel agree bit for bit (y and the sum)
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(rows + cols)
+    x = torch.randn(rows, cols, generator=g, device=dev).to(dtype)
+    r = torch.randn(rows, cols, generator=g, device=dev).to(dtype)
+    w = torch.randn(cols, generator=g, device=dev).to(dtype)
+    y0, s0 = hfa.rmsnorm(x, w, 1e-6, residual=r)
+    for _ in range(2):
+        y, s = hfa.rmsnorm(x, w, 1e-6, residual=r)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y0) and torch.equal(s, s0)
