@@ -160,6 +160,10 @@ def time_gpu(w, steps: int, warmup: int, ramp_s: float = CLOCK_RAMP_S):
         "frac": round(tflops / peak, 4),
         "traffic": None if traffic is None else int(traffic["hbm_bytes_per_launch"]),
         "algorithmic_bytes": algorithmic_bytes(w),
+        # HBM rates over the measured step: counted traffic (when taken on these sources) and
+        # the algorithmic Q, K, V, O and LSE bytes
+        "traffic_gbs": None if traffic is None else round(traffic["hbm_bytes_per_launch"] / (ms * 1e6), 1),
+        "algorithmic_gbs": round(algorithmic_bytes(w) / (ms * 1e6), 1),
         "kernel": kernel_key(w),
     }
     if w.dtype == "f32":
@@ -718,7 +722,10 @@ def summarize_trace(n: int, trace_dir: str, trace_json: str, bench_json: str | N
                   f"| WRITE_SIZE | {t['write']['kernel_kib_per_dispatch']:.1f} | {t['write']['copy_kib']:.1f} | "
                   f"{t['write']['bytes_per_launch']:.0f} |", "",
                   f"HBM traffic per launch: {t['hbm_bytes_per_launch'] / 1e6:.1f} MB; algorithmic (Q, K, V read "
-                  f"once, O and LSE written once): {t['algorithmic_bytes'] / 1e6:.1f} MB.", ""]
+                  f"once, O and LSE written once): {t['algorithmic_bytes'] / 1e6:.1f} MB.",
+                  f"Over the traced average kernel time: {t['hbm_bytes_per_launch'] / avg_timed:.1f} GB/s of counted "
+                  f"traffic ({t['hbm_bytes_per_launch'] / avg_timed / HBM_PEAK_GBS:.3f} of the {HBM_PEAK_GBS:.0f} GB/s "
+                  f"HBM peak), {t['algorithmic_bytes'] / avg_timed:.1f} GB/s of algorithmic bytes.", ""]
     lines.append(f"Kernel source digest when taken: `{kernel_source_digest()}`.")
     path = os.path.join(ROOT, "profiles", kernel_profile_name(w) + ".md")
     with open(path, "w") as f:
