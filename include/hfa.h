@@ -33,6 +33,12 @@
  * products on bf16 matrix cores with fp32 accumulation, softmax in fp32,
  * P rounded to bf16 (round-to-nearest-even) for P V, O rounded to bf16 once.
  *
+ * Input domain.  Q, K, V and scale are finite (NaN or infinite entries give
+ * unspecified results).  HFA_BF16 accumulates scores in fp32, so every
+ * |scale q.k| must stay within the fp32 range (about 3.4e38).  HFA_F32 forms
+ * scores in fp64 and has no such limit; only an LSE whose value exceeds the
+ * fp32 range is returned as +inf.
+ *
  * Ownership.  The caller owns every buffer; hfa_attn_fwd allocates nothing,
  * keeps no state between calls and never holds an N x N buffer.  All pointers
  * passed to it are device pointers on the current HIP device.  The graph
