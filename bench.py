@@ -122,6 +122,19 @@ def warm_up(launch, warmup: int, ramp_s: float) -> None:
         torch.cuda.synchronize()
 
 
+def attn_workspace(w, dev):
+    """The workspace the library asks for on this workload (fp32 shapes whose key tiles
+    are shared by enough workgroups: K and V formatted once per call; bf16: a key
+    split), allocated once outside the timed region, or None."""
+    import torch
+
+    import fa2_fwd_amd as hfa
+
+    code = hfa.HFA_F32 if w.dtype == "f32" else hfa.HFA_BF16
+    need = hfa.hfa_attn_fwd_workspace_size(code, w.B, w.H, w.N, w.d, 0)
+    return torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else None
+
+
 def time_gpu(w, steps: int, warmup: int, ramp_s: float = CLOCK_RAMP_S):
     import torch
 
@@ -134,14 +147,15 @@ def time_gpu(w, steps: int, warmup: int, ramp_s: float = CLOCK_RAMP_S):
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    warm_up(lambda: hfa.attn_fwd(q, k, v, w.scale, out=o, lse=lse, stream=stream), warmup, ramp_s)
+    ws = attn_workspace(w, dev)
+    warm_up(lambda: hfa.attn_fwd(q, k, v, w.scale, out=o, lse=lse, stream=stream, workspace=ws), warmup, ramp_s)
     # One event before each launch and one after the last, all on the launch
     # stream: their span is the timed region, their gaps the per-launch times.
     events = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     t0 = time.perf_counter()
     for i in range(steps):
         events[i].record(stream)
-        hfa.attn_fwd(q, k, v, w.scale, out=o, lse=lse, stream=stream)
+        hfa.attn_fwd(q, k, v, w.scale, out=o, lse=lse, stream=stream, workspace=ws)
     events[steps].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -411,13 +425,14 @@ def observed_sclk(w, seconds: float):
             time.sleep(0.005)
 
     th = threading.Thread(target=sampler, daemon=True)
-    hfa.attn_fwd(q, k, v, w.scale)
+    ws = attn_workspace(w, dev)
+    hfa.attn_fwd(q, k, v, w.scale, workspace=ws)
     torch.cuda.synchronize()
     th.start()
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < seconds:
         for _ in range(20):
-            hfa.attn_fwd(q, k, v, w.scale)
+            hfa.attn_fwd(q, k, v, w.scale, workspace=ws)
         torch.cuda.synchronize()
     stop.set()
     th.join()
@@ -554,9 +569,10 @@ def profile_pass(w, launches: int, warmup: int, ramp_s: float) -> None:
     o = torch.empty_like(q)
     lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    warm_up(lambda: hfa.attn_fwd(q, k, v, w.scale, out=o, lse=lse, stream=stream), warmup, ramp_s)
+    ws = attn_workspace(w, dev)
+    warm_up(lambda: hfa.attn_fwd(q, k, v, w.scale, out=o, lse=lse, stream=stream, workspace=ws), warmup, ramp_s)
     for _ in range(launches):
-        hfa.attn_fwd(q, k, v, w.scale, out=o, lse=lse, stream=stream)
+        hfa.attn_fwd(q, k, v, w.scale, out=o, lse=lse, stream=stream, workspace=ws)
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()

@@ -271,9 +271,11 @@ def attn_fwd(q, k, v, scale: float | None = None, out=None, lse=None, stream=Non
     ([B,H,N] float32) may be given to write into caller buffers.  The kernels are
     enqueued on ``stream`` (default: torch's current stream) and not waited for.
     ``splits`` is the key split (hfa_attn_fwd_split): 0 lets the library choose (bf16
-    shapes too small to fill the GPU split their keys), 1 never splits.  A split call
-    needs a workspace of hfa_attn_fwd_workspace_size bytes: ``workspace`` (a device
-    tensor) if given, else one from torch's allocator, kept alive for ``stream``.
+    shapes too small to fill the GPU split their keys; fp32 shapes whose key tiles are
+    shared by enough workgroups format K and V once per call), 1 never splits (fp32:
+    always formats K and V once per call).  Such a call needs a workspace of
+    hfa_attn_fwd_workspace_size bytes: ``workspace`` (a device tensor) if given, else
+    one from torch's allocator, kept alive for ``stream``.
     Raises ValueError on dtype, shape, device or contiguity mismatch and HfaError on a
     library error.
     """

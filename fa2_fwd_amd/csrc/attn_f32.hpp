@@ -88,6 +88,24 @@ struct F32Tile {
   static constexpr int VITEMS = (KT / 32) * 4 * D / NT;
   static constexpr int MISCB = 2 * (KTILEB + VTILEB);  // per-wave key statistics for the exactness check
   static constexpr int LDS_BYTES = MISCB + NW * (CH + 1) * 4;
+  // Pre-formatted tiles (f32_pack_kernel), PACKB bytes each: the K image of
+  // an LDS buffer followed by the tile's key statistics (CH floats and one
+  // int), padded to KPADB, then the V image (VPADB), each part a whole number
+  // of rounds of 16-byte copies by all NT threads.  In LDS the two K parts
+  // come first (buffer b at b KPADB) and the two V parts after them, so that
+  // every K read of either buffer lies within the 64 KiB an LDS instruction's
+  // immediate offset reaches from one base.
+  static constexpr int STATB = 4 * (CH + 1);
+  static constexpr int ROUNDB = 16 * NT;
+  static constexpr int KPADB = (KTILEB + STATB + ROUNDB - 1) / ROUNDB * ROUNDB;
+  static constexpr int VPADB = (VTILEB + ROUNDB - 1) / ROUNDB * ROUNDB;
+  static constexpr int PACKB = KPADB + VPADB;
+  static constexpr int PCOPIES = PACKB / ROUNDB;  // 16-byte copies per thread per tile
+  static constexpr int KCOPIES = KPADB / ROUNDB;  // of which into the K part
+  static constexpr int P_MISCB = 2 * PACKB;
+  static constexpr int P_LDS_BYTES = P_MISCB + NW * (CH + 1) * 4;
+  static_assert(KTILEB % 16 == 0, "the statistics start 16-byte aligned");
+  static_assert(2 * KPADB <= 65536, "both K parts lie within 64 KiB");
   static_assert((KT * CH) % NT == 0, "tile chunks must divide evenly over the threads");
   static_assert(KT % 32 == 0, "key tile is a whole number of 32-key chunks");
   static_assert(CH == 16 || CH == 32, "a K row spans 16 or 32 lanes (d = 64 or 128)");
@@ -315,11 +333,182 @@ __device__ __forceinline__ void exact_rows_impl(const float* __restrict__ Qh, co
   }
 }
 
+// ---- S^T = K Q^T from the int8 slices for one 16-key block (slices ks of
+// the block's key rows, ek their exponents) and one 16-query block (slices
+// qsb, exponent eqb): the slice products with a + b = t accumulate exactly in
+// acc_t (|acc_t| < 2^21), then s = 2^(eq + ek - 12) sum_t acc_t 2^(-7t) in
+// fp64, combined as 2^-35 (acc01 2^28 + acc23 2^14 + acc45) with
+// acc01 = 2^7 acc_0 + acc_1 etc. formed exactly in int32.
 template <class T>
+__device__ __forceinline__ f64x4 score_block_f32(const i32x4 (&ks)[T::D / 64][T::NSL],
+                                                 const u32x4 (&qsb)[T::D / 64][T::NSL], i32x4 ek, int eqb) {
+  i32x4 at[2 * T::NSL - 4];
+#pragma unroll
+  for (int t = 0; t < 2 * T::NSL - 4; ++t) at[t] = i32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int h = 0; h < T::D / 64; ++h)
+#pragma unroll
+    for (int a2 = 0; a2 < T::NSL; ++a2)
+#pragma unroll
+      for (int b2 = 0; b2 < T::NSL; ++b2)
+        if (a2 + b2 <= 5)
+          at[a2 + b2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ks[h][a2], __builtin_bit_cast(i32x4, qsb[h][b2]),
+                                                              at[a2 + b2], 0, 0, 0);
+  f64x4 s;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int a01 = at[0][r] * 128 + at[1][r];
+    const int a23 = at[2][r] * 128 + at[3][r];
+    const int a45 = at[4][r] * 128 + at[5][r];
+    const double x = fma(static_cast<double>(a01), 268435456.0,
+                         fma(static_cast<double>(a23), 16384.0, static_cast<double>(a45)));
+    s[r] = __builtin_amdgcn_ldexp(x, eqb + ek[r] - 47);
+  }
+  return s;
+}
+
+// ---- online softmax update of one 16-query block over a key tile: scores
+// sb, weights pb out; running max m2 (log2 units), denominator l and output
+// sums accb updated.
+template <class T>
+__device__ __forceinline__ void softmax_block_f32(const f64x4 (&sb)[T::KT / 16], f32x4 (&pb)[T::KT / 16], double& m2,
+                                                  double& l, f32x4 (&accb)[T::D / 16], double c2) {
+  double mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < T::KT / 16; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mx = fmax(mx, sb[kb][r]);
+  mx = max_xor<16>(mx);
+  mx = max_xor<32>(mx);
+  // log2-domain running max, rounded up to an integer: exact rescale factors.
+  const double m_new = fmax(m2, ceil(mx * c2));
+  const float alpha = exp2_hw(static_cast<float>(m2 - m_new));  // 0 on the first tile
+  float ts = 0.0f;
+#pragma unroll
+  for (int kb = 0; kb < T::KT / 16; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x = exp2_hw(static_cast<float>(fma(sb[kb][r], c2, -m_new)));
+      pb[kb][r] = x;
+      ts += x;
+    }
+  l = l * static_cast<double>(alpha) + static_cast<double>(ts);
+  m2 = m_new;
+#pragma unroll
+  for (int n = 0; n < T::D / 16; ++n) accb[n] *= alpha;
+}
+
+// Formats K and V once per call for the packed attention kernel: workgroup
+// (bh, j) writes tile j of head bh exactly as the attention kernel's own
+// staging leaves it in an LDS buffer (int8 slice planes and row exponents of
+// K, bf16 pieces of V, keys at or past N zero), followed by the tile's key
+// statistics for the exactness check: per column chunk the largest L1 norm
+// of a key row's chunk, then the largest key exponent.  The thread mapping
+// and the arithmetic are those of the staging, so both paths feed the matrix
+// cores the same bytes and give identical results.
+template <class T>
+__global__ __launch_bounds__(T::NT) void f32_pack_kernel(const float* __restrict__ K, const float* __restrict__ V,
+                                                         char* __restrict__ ws, int N, int ntiles) {
+  constexpr int D = T::D, KT = T::KT, CH = T::CH;
+  __shared__ float red_a[T::NW][CH];
+  __shared__ int red_e[T::NW];
+  const int tid = thread_id();
+  const int lane = tid & 63, wave = tid >> 6;
+  const int blk = group_id();
+  const int bh = uniform_sgpr(blk / ntiles);
+  const int j = uniform_sgpr(blk - bh * ntiles);
+  const size_t head = static_cast<size_t>(bh) * static_cast<size_t>(N) * D;
+  const float* Kh = K + head;
+  const float* Vh = V + head;
+  char* kt = ws + static_cast<size_t>(blk) * T::PACKB;
+  char* vt = kt + T::KPADB;
+
+  float kmax_a = 0.0f;
+  int kmax_e = -1024;
+#pragma unroll
+  for (int u = 0; u < T::LOADS; ++u) {
+    const int idx = tid + u * T::NT;
+    const int row = stage_row<D>(idx / CH), ch = idx % CH;
+    const int key = j * KT + row;
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (key < N) x = *reinterpret_cast<const f32x4*>(Kh + (key * D + ch * 4));
+    float mx = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+    kmax_a = fmaxf(kmax_a, (fabsf(x[0]) + fabsf(x[1])) + (fabsf(x[2]) + fabsf(x[3])));
+    mx = max_row16(mx);
+    if constexpr (CH == 32) mx = max_xor16_f32(mx);
+    const int e = row_exponent(mx);
+    uint32_t w[T::NSL];
+    slice5(x, e, w);
+    const int off = row * T::KSROW + (((ch >> 2) ^ kswz<D>(row)) << 4) + 4 * (ch & 3);
+#pragma unroll
+    for (int a2 = 0; a2 < T::NSL; ++a2) *reinterpret_cast<uint32_t*>(kt + off + a2 * T::KSPLANEB) = w[a2];
+    if (ch == 0) *reinterpret_cast<int*>(kt + T::KEXPB + 4 * row) = e;
+    kmax_e = max(kmax_e, e);
+  }
+  // V items as in the staging: 32-key chunk c, key class g8, column vcol;
+  // three bf16 pieces by truncation, pieces of two keys per 32-bit word.
+#pragma unroll
+  for (int it = 0; it < T::VITEMS; ++it) {
+    const int item = tid + it * T::NT;
+    const int vcol = item % D, cg = item / D;
+    const int c = cg >> 2, g8 = cg & 3;
+    float xv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int key = j * KT + 32 * c + 16 * (i >> 2) + 4 * g8 + (i & 3);
+      xv[i] = key < N ? Vh[key * D + vcol] : 0.0f;
+    }
+    u32x4 w1, w2, w3;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      uint32_t b1[2], b2[2], b3[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float x = xv[2 * h + e];
+        b1[e] = __float_as_uint(x) & 0xffff0000u;
+        const float r = x - __uint_as_float(b1[e]);
+        b2[e] = __float_as_uint(r) & 0xffff0000u;
+        b3[e] = __float_as_uint(r - __uint_as_float(b2[e]));
+      }
+      w1[h] = (b1[0] >> 16) | b1[1];
+      w2[h] = (b2[0] >> 16) | b2[1];
+      w3[h] = (b3[0] >> 16) | (b3[1] & 0xffff0000u);
+    }
+    *reinterpret_cast<u32x4*>(vt + item * 16) = w1;
+    *reinterpret_cast<u32x4*>(vt + T::VPLANEB + item * 16) = w2;
+    *reinterpret_cast<u32x4*>(vt + 2 * T::VPLANEB + item * 16) = w3;
+  }
+  // The tile's statistics: lanes l, l + CH, ... of a wave share a column chunk.
+#pragma unroll
+  for (int m = 1; m < 64; m *= 2) {
+    kmax_e = max(kmax_e, __shfl_xor(kmax_e, m));
+    if (m >= CH) kmax_a = fmaxf(kmax_a, __shfl_xor(kmax_a, m));
+  }
+  if (lane < CH) red_a[wave][lane] = kmax_a;
+  if (lane == 0) red_e[wave] = kmax_e;
+  __syncthreads();
+  char* st = kt + T::KTILEB;
+  if (tid < CH) {
+    float m = 0.0f;
+#pragma unroll
+    for (int w = 0; w < T::NW; ++w) m = fmaxf(m, red_a[w][tid]);
+    reinterpret_cast<float*>(st)[tid] = m;
+  } else if (tid == CH) {
+    int m = -1024;
+#pragma unroll
+    for (int w = 0; w < T::NW; ++w) m = max(m, red_e[w]);
+    reinterpret_cast<int*>(st)[CH] = m;
+  }
+}
+
+// PACKED: K and V tiles come pre-formatted from f32_pack_kernel (`packed`,
+// [B*H][ntiles][PACKB]) and are copied into LDS as they are, with no staging
+// arithmetic; otherwise the workgroup formats every tile itself.
+template <class T, bool PACKED = false>
 __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int N, int n_qt, int total_wg, double c2,
-    int q_mode) {
+    int q_mode, const char* __restrict__ packed) {
   constexpr int D = T::D, QB = T::QB, KT = T::KT;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -331,7 +520,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
   // interval instead of at its end (and request the one after it straight
   // away), so their staging work overlaps the other wave's score products and
   // the other wave's staging overlaps their P V products.
-  constexpr bool kSkew = HFA_F32_SKEW && T::NW == 8;
+  constexpr bool kSkew = HFA_F32_SKEW && T::NW == 8 && !PACKED;
   const bool late = kSkew && __builtin_amdgcn_readfirstlane(tid >> 6) >= T::NW / 2;
 
   // Workgroup-uniform indices, kept in scalar registers (the division runs on
@@ -512,10 +701,37 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
   };
 
   const int ntiles = (N + KT - 1) / KT;
-  stage_load(0, std::false_type{});
-  stage_store(0);
-  if (late && ntiles > 1) stage_load(1, std::false_type{});
-  __syncthreads();
+  // Packed tiles: buffer b holds a tile's K part at smem + b * KPADB and its V
+  // part at smem + 2 KPADB + b * VPADB; each of the NT threads copies 16 bytes
+  // per round, wave w's lanes filling 1 KiB of the round.
+  const char* blobs = PACKED ? packed + static_cast<size_t>(bh) * static_cast<size_t>(ntiles) * T::PACKB : nullptr;
+  // The round moves the scalar source and LDS bases; the lane's offset is one
+  // register, recomputed from an opaque thread index (not kept across the loop).
+  // The LDS addresses are scalar: the buffer base plus this wave's 1 KiB.
+  const uint32_t wave_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)smem)) +
+                            1024u * static_cast<uint32_t>(uniform_sgpr(tid >> 6));
+  auto copy_tile = [&](int jj, int b) __attribute__((always_inline)) {
+    const char* src = blobs + static_cast<size_t>(jj) * T::PACKB;
+    const uint32_t kdst = wave_lds + b * T::KPADB;
+    const uint32_t vdst = wave_lds + 2 * T::KPADB + b * T::VPADB;
+    int voff = tid;
+    asm volatile("" : "+v"(voff));
+    voff *= 16;
+#pragma unroll
+    for (int u = 0; u < T::PCOPIES; ++u)
+      dma16_to(src + u * T::ROUNDB, voff,
+               u < T::KCOPIES ? kdst + u * T::ROUNDB : vdst + (u - T::KCOPIES) * T::ROUNDB);
+  };
+  if constexpr (PACKED) {
+    copy_tile(0, 0);
+    vmcnt_wait<0>();
+    __syncthreads();
+  } else {
+    stage_load(0, std::false_type{});
+    stage_store(0);
+    if (late && ntiles > 1) stage_load(1, std::false_type{});
+    __syncthreads();
+  }
 
   // One key tile.  buf is the LDS buffer of tile j (j & 1), a compile-time
   // constant in the unrolled loop below so that the buffer offset folds into
@@ -533,7 +749,9 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
       else
         return static_cast<int>(decltype(buf_tag)::value);
     }();
-    if constexpr (kSkew) {
+    if constexpr (PACKED) {
+      if (steady || j + 1 < ntiles) copy_tile(j + 1, buf ^ 1);
+    } else if constexpr (kSkew) {
       if (late) {
         // the late waves' half of tile j + 1, requested at the start of tile
         // j - 1, then their request for tile j + 2
@@ -554,8 +772,8 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
       else if (j + 1 < ntiles)
         stage_load(j + 1, std::false_type{});
     }
-    const char* kt = smem + buf * (T::KTILEB + T::VTILEB);
-    const char* vt = kt + T::KTILEB;
+    const char* kt = smem + buf * (PACKED ? T::KPADB : T::KTILEB + T::VTILEB);
+    const char* vt = PACKED ? smem + 2 * T::KPADB + buf * T::VPADB : kt + T::KTILEB;
 
     // ---- S^T = K Q^T from the int8 slices: for each 16-key block, the slice
     // products with a + b = t accumulate exactly in acc_t (|acc_t| < 2^21),
@@ -563,87 +781,63 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
     // 2^-35 (acc01 2^28 + acc23 2^14 + acc45) with acc01 = 2^7 acc_0 + acc_1
     // etc. formed exactly in int32.
     f64x4 s[QB][KT / 16];
-#pragma unroll
-    for (int kb = 0; kb < KT / 16; ++kb) {
-      i32x4 ks[D / 64][T::NSL];
-#pragma unroll
-      for (int h = 0; h < D / 64; ++h)
-#pragma unroll
-        for (int a2 = 0; a2 < T::NSL; ++a2)
-          ks[h][a2] = __builtin_bit_cast(
-              i32x4, lds_load16(kt, a2 * T::KSPLANEB + (kb * 16 + i16) * T::KSROW + (((4 * h + g) ^ kswz<D>(i16)) << 4)));
-      const i32x4 ek = __builtin_bit_cast(i32x4, lds_load16(kt, T::KEXPB + (kb * 16 + 4 * g) * 4));
+    f32x4 p[QB][KT / 16];
+    // ---- keys past the end get score -inf
+    const int key0 = j * KT;
+    if constexpr (PACKED && QB > 1) {
+      // One query block at a time (its scores, then its softmax): only one
+      // block's fp64 scores are live, and the softmax of a block can overlap
+      // the score products of the next.  The K slices are read once per block.
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        i32x4 at[2 * T::NSL - 4];
 #pragma unroll
-        for (int t = 0; t < 2 * T::NSL - 4; ++t) at[t] = i32x4{0, 0, 0, 0};
+        for (int kb = 0; kb < KT / 16; ++kb) {
+          i32x4 ks[D / 64][T::NSL];
+#pragma unroll
+          for (int h = 0; h < D / 64; ++h)
+#pragma unroll
+            for (int a2 = 0; a2 < T::NSL; ++a2)
+              ks[h][a2] = __builtin_bit_cast(i32x4, lds_load16(kt, a2 * T::KSPLANEB + (kb * 16 + i16) * T::KSROW +
+                                                                       (((4 * h + g) ^ kswz<D>(i16)) << 4)));
+          const i32x4 ek = __builtin_bit_cast(i32x4, lds_load16(kt, T::KEXPB + (kb * 16 + 4 * g) * 4));
+          s[qb][kb] = score_block_f32<T>(ks, qs[qb], ek, eq[qb]);
+        }
+        if (!steady && key0 + KT > N) {
+#pragma unroll
+          for (int kb = 0; kb < KT / 16; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (key0 + kb * 16 + 4 * g + r >= N) s[qb][kb][r] = -INFINITY;
+        }
+        softmax_block_f32<T>(s[qb], p[qb], m2[qb], l_run[qb], acc[qb], c2);
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KT / 16; ++kb) {
+        i32x4 ks[D / 64][T::NSL];
 #pragma unroll
         for (int h = 0; h < D / 64; ++h)
 #pragma unroll
           for (int a2 = 0; a2 < T::NSL; ++a2)
+            ks[h][a2] = __builtin_bit_cast(
+                i32x4, lds_load16(kt, a2 * T::KSPLANEB + (kb * 16 + i16) * T::KSROW + (((4 * h + g) ^ kswz<D>(i16)) << 4)));
+        const i32x4 ek = __builtin_bit_cast(i32x4, lds_load16(kt, T::KEXPB + (kb * 16 + 4 * g) * 4));
 #pragma unroll
-            for (int b2 = 0; b2 < T::NSL; ++b2)
-              if (a2 + b2 <= 5)
-                at[a2 + b2] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ks[h][a2], __builtin_bit_cast(i32x4, qs[qb][h][b2]),
-                                                                    at[a2 + b2], 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int a01 = at[0][r] * 128 + at[1][r];
-          const int a23 = at[2][r] * 128 + at[3][r];
-          const int a45 = at[4][r] * 128 + at[5][r];
-          const double x = fma(static_cast<double>(a01), 268435456.0,
-                               fma(static_cast<double>(a23), 16384.0, static_cast<double>(a45)));
-          s[qb][kb][r] = __builtin_amdgcn_ldexp(x, eq[qb] + ek[r] - 47);
-        }
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = score_block_f32<T>(ks, qs[qb], ek, eq[qb]);
       }
-    }
-
-    // ---- exact scores for a tile whose slice bound is too loose: fp64
-    // products of the fp32 values (exact) summed in fp64, read from memory
-    // (the tile was just staged, so it is in the caches).  Rare: the five
-    // evaluation workloads never take it.
-    // ---- keys past the end get score -inf
-    const int key0 = j * KT;
-    if (!steady && key0 + KT > N) {
+      if (!steady && key0 + KT > N) {
 #pragma unroll
-      for (int kb = 0; kb < KT / 16; ++kb)
+        for (int kb = 0; kb < KT / 16; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = key0 + kb * 16 + 4 * g + r;
-          if (key >= N)
+          for (int r = 0; r < 4; ++r) {
+            const int key = key0 + kb * 16 + 4 * g + r;
+            if (key >= N)
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[qb][kb][r] = -INFINITY;
-        }
-    }
-
-    // ---- online softmax update
-    f32x4 p[QB][KT / 16];
+              for (int qb = 0; qb < QB; ++qb) s[qb][kb][r] = -INFINITY;
+          }
+      }
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      double mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < KT / 16; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mx = fmax(mx, s[qb][kb][r]);
-      mx = max_xor<16>(mx);
-      mx = max_xor<32>(mx);
-      // log2-domain running max, rounded up to an integer: exact rescale factors.
-      const double m_new = fmax(m2[qb], ceil(mx * c2));
-      const float alpha = exp2_hw(static_cast<float>(m2[qb] - m_new));  // 0 on the first tile
-      float ts = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < KT / 16; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float x = exp2_hw(static_cast<float>(fma(s[qb][kb][r], c2, -m_new)));
-          p[qb][kb][r] = x;
-          ts += x;
-        }
-      l_run[qb] = l_run[qb] * static_cast<double>(alpha) + static_cast<double>(ts);
-      m2[qb] = m_new;
-#pragma unroll
-      for (int n = 0; n < D / 16; ++n) acc[qb][n] *= alpha;
+      for (int qb = 0; qb < QB; ++qb) softmax_block_f32<T>(s[qb], p[qb], m2[qb], l_run[qb], acc[qb], c2);
     }
 
     // ---- O^T += V^T P^T on the bf16 matrix cores, six piece products per
@@ -688,7 +882,16 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
       }
     }
 
-    if constexpr (kSkew) {
+    if constexpr (PACKED) {
+      // the tile's key statistics, then the wait for this wave's copies of
+      // the next tile
+      const char* st = kt + T::KTILEB;
+      kmax_a = fmaxf(kmax_a, reinterpret_cast<const float*>(st)[lane % T::CH]);
+      kmax_e = max(kmax_e, reinterpret_cast<const int*>(st)[T::CH]);
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    } else if constexpr (kSkew) {
       if (!late && (steady || j + 1 < ntiles)) stage_store(buf ^ 1);
       // LDS traffic only: the late waves' requests for tile j + 2 stay in flight
       __builtin_amdgcn_sched_barrier(0);
@@ -737,7 +940,7 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
       kmax_e = max(kmax_e, __shfl_xor(kmax_e, m));
       if (m >= T::CH) kmax_a = fmaxf(kmax_a, __shfl_xor(kmax_a, m));
     }
-    int* kst = reinterpret_cast<int*>(smem + T::MISCB);
+    int* kst = reinterpret_cast<int*>(smem + (PACKED ? T::P_MISCB : T::MISCB));
     if (lane_after < T::CH) kst[wave_after * T::CH + lane_after] = __float_as_int(kmax_a);
     if (lane_after == 0) kst[T::NW * T::CH + wave_after] = kmax_e;
     lds_barrier_f32();

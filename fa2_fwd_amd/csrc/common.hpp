@@ -63,6 +63,63 @@ __device__ __forceinline__ float add_xor32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// One 16-byte-per-lane HBM -> LDS copy (global_load_lds_dwordx4): lane l
+// reads base + voff(l) and writes LDS bytes [lds + 16 l, lds + 16 l + 16).
+// base and lds must be wave-uniform.  Issued through inline assembly so that
+// the compiler does not make every later LDS read wait for it; completion is
+// ordered explicitly with vmcnt_wait and the workgroup barriers.
+#ifndef HFA_DMA_ASM
+#define HFA_DMA_ASM 1
+#endif
+__device__ __forceinline__ void dma16(const char* base, int voff, char* lds) {
+#if HFA_DMA_ASM
+  // readfirstlane returns int: every half goes through uint32_t before it is
+  // widened, so the low half is never sign-extended into the high word.
+  const uint32_t lds_addr = static_cast<uint32_t>(
+      __builtin_amdgcn_readfirstlane(static_cast<int>(reinterpret_cast<uintptr_t>((lds_void*)lds))));
+  const uint64_t b = reinterpret_cast<uintptr_t>(base);
+  const uint32_t b_lo = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b))));
+  const uint32_t b_hi = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(b >> 32))));
+  const uint64_t sbase = (static_cast<uint64_t>(b_hi) << 32) | static_cast<uint64_t>(b_lo);
+  // M0 carries the LDS destination; its previous value is restored, so the
+  // statement leaves every register the compiler may rely on unchanged.  A
+  // scalar write of M0 needs one wait state before a load to LDS reads it;
+  // the compiler cannot see into the statement, so the s_nop is written here.
+  // (The scalar operands come from readfirstlane, and a VALU write of an SGPR
+  // needs five wait states before a vector-memory read of it; the compiler
+  // hoists them out of the key loop, far from any use.)
+  uint32_t saved_m0;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved_m0)
+      : "s"(lds_addr), "v"(voff), "s"(sbase)
+      : "memory");
+#else
+  __builtin_amdgcn_global_load_lds(base + voff, (lds_void*)lds, 16, 0, 0);
+#endif
+}
+
+// The same copy with operands the caller keeps in scalar registers: a
+// wave-uniform global base and the LDS destination as a uniform LDS address
+// (no generic-pointer conversion and no readfirstlane here).  The caller
+// forms both with scalar arithmetic, so no vector instruction writes them.
+__device__ __forceinline__ void dma16_to(const char* base, int voff, uint32_t lds_addr) {
+  uint32_t saved_m0;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %2, %3\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved_m0)
+      : "s"(lds_addr), "v"(voff), "s"(base)
+      : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void vmcnt_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 __device__ __forceinline__ void lds_store16(char* lds, int byte_off, u32x4 v) {
   *reinterpret_cast<u32x4*>(lds + byte_off) = v;
 }

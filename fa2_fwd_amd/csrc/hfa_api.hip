@@ -191,22 +191,41 @@ hfa_status launch_bf16(const void* q, const void* k, const void* v, void* o, flo
   return HFA_OK;
 }
 
+// Bytes of pre-formatted K/V tiles (f32_pack_kernel) for B*H heads of N keys.
+template <class T>
+int64_t f32_pack_bytes(int64_t BH, int64_t N) {
+  return BH * ((N + T::KT - 1) / T::KT) * T::PACKB;
+}
+
+// ws: workspace of at least f32_pack_bytes<T> bytes for the packed path
+// (K and V formatted once, then copied into LDS as they are), or null for the
+// path that formats every tile in every workgroup.
 template <class T>
 hfa_status launch_f32(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH,
-                      int64_t N, float scale, hipStream_t stream, bool launch) {
-  static std::once_flag flag;
-  static hipError_t err = hipSuccess;
-  auto kernel = attn_fwd_f32_kernel<T>;
+                      int64_t N, float scale, hipStream_t stream, bool launch, void* ws = nullptr) {
+  static std::once_flag flag, flag_packed;
+  static hipError_t err = hipSuccess, err_packed = hipSuccess;
+  auto kernel = attn_fwd_f32_kernel<T, false>;
+  auto kernel_packed = attn_fwd_f32_kernel<T, true>;
   if (ensure_lds(kernel, T::LDS_BYTES, flag, err) != HFA_OK) return HFA_ERR_LAUNCH;
+  if (ensure_lds(kernel_packed, T::P_LDS_BYTES, flag_packed, err_packed) != HFA_OK) return HFA_ERR_LAUNCH;
   if (!launch) return HFA_OK;
   const int64_t n_qt = (N + T::BR - 1) / T::BR;
   const int64_t total = BH * n_qt;
-  if (total > INT_MAX) return HFA_ERR_SHAPE;
+  const int64_t ntiles = (N + T::KT - 1) / T::KT;
+  if (total > INT_MAX || BH * ntiles > INT_MAX) return HFA_ERR_SHAPE;
   const ScaleArgs sa = split_scale(scale);
-  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(total)), dim3(T::NT), T::LDS_BYTES, stream,
-                     static_cast<const float*>(q), static_cast<const float*>(k),
-                     static_cast<const float*>(v), static_cast<float*>(o), lse, static_cast<int>(N),
-                     static_cast<int>(n_qt), static_cast<int>(total), sa.c2, sa.q_mode);
+  if (ws) {
+    hipLaunchKernelGGL(f32_pack_kernel<T>, dim3(static_cast<unsigned>(BH * ntiles)), dim3(T::NT), 0, stream,
+                       static_cast<const float*>(k), static_cast<const float*>(v), static_cast<char*>(ws),
+                       static_cast<int>(N), static_cast<int>(ntiles));
+    if (hipGetLastError() != hipSuccess) return HFA_ERR_LAUNCH;
+  }
+  hipLaunchKernelGGL(ws ? kernel_packed : kernel, dim3(static_cast<unsigned>(total)), dim3(T::NT),
+                     ws ? T::P_LDS_BYTES : T::LDS_BYTES, stream, static_cast<const float*>(q),
+                     static_cast<const float*>(k), static_cast<const float*>(v), static_cast<float*>(o), lse,
+                     static_cast<int>(N), static_cast<int>(n_qt), static_cast<int>(total), sa.c2, sa.q_mode,
+                     static_cast<const char*>(ws));
   return hipGetLastError() == hipSuccess ? HFA_OK : HFA_ERR_LAUNCH;
 }
 
@@ -236,7 +255,8 @@ hfa_status validate(const void* q, const void* k, const void* v, const void* o, 
 }
 
 // Kernel selection for a validated call; enqueues it on `stream` when launch.
-// ks / work: the key split of a bf16 call and its workspace.
+// ks / work: the key split of a bf16 call and its workspace; for fp32, work
+// is the packed path's workspace (or null).
 hfa_status dispatch(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH, int64_t N,
                     int64_t d, float scale, hfa_dtype dtype, hipStream_t st, bool launch, KeySplit ks = {1, 0},
                     void* work = nullptr) {
@@ -248,12 +268,40 @@ hfa_status dispatch(const void* q, const void* k, const void* v, void* o, float*
   }
   if (d == 64) {
     switch (f32_d64_tiling(BH, N)) {
-      case 2: return launch_f32<F32D64Big>(q, k, v, o, lse, BH, N, scale, st, launch);
-      case 1: return launch_f32<F32D64Small>(q, k, v, o, lse, BH, N, scale, st, launch);
-      default: return launch_f32<F32D64Tiny>(q, k, v, o, lse, BH, N, scale, st, launch);
+      case 2: return launch_f32<F32D64Big>(q, k, v, o, lse, BH, N, scale, st, launch, work);
+      case 1: return launch_f32<F32D64Small>(q, k, v, o, lse, BH, N, scale, st, launch, work);
+      default: return launch_f32<F32D64Tiny>(q, k, v, o, lse, BH, N, scale, st, launch, work);
     }
   }
-  return launch_f32<F32D128>(q, k, v, o, lse, BH, N, scale, st, launch);
+  return launch_f32<F32D128>(q, k, v, o, lse, BH, N, scale, st, launch, work);
+}
+
+// Formatting K and V once per call pays when at least this many query-row
+// tiles (workgroups) of a head share each key tile: each of them would
+// otherwise format every key tile itself.  Measured break-even on MI355X at
+// about 8 (B*H=32, N=2048 and N=1024, d=64).
+constexpr int64_t kPackMinRowTiles = 8;
+
+// The fp32 tiling's query rows per workgroup.
+int64_t f32_block_rows(int64_t BH, int64_t N, int64_t d) {
+  if (d == 128) return F32D128::BR;
+  const int t = f32_d64_tiling(BH, N);
+  return t == 2 ? F32D64Big::BR : t == 1 ? F32D64Small::BR : F32D64Tiny::BR;
+}
+
+bool f32_pack_pays(int64_t BH, int64_t N, int64_t d) {
+  const int64_t br = f32_block_rows(BH, N, d);
+  return (N + br - 1) / br >= kPackMinRowTiles;
+}
+
+// Workspace bytes of the packed fp32 path for the tiling the call would use.
+int64_t f32_workspace_bytes(int64_t BH, int64_t N, int64_t d) {
+  if (d == 128) return f32_pack_bytes<F32D128>(BH, N);
+  switch (f32_d64_tiling(BH, N)) {
+    case 2: return f32_pack_bytes<F32D64Big>(BH, N);
+    case 1: return f32_pack_bytes<F32D64Small>(BH, N);
+    default: return f32_pack_bytes<F32D64Tiny>(BH, N);
+  }
 }
 
 // ---- allocation-free key split ----------------------------------------------
@@ -340,8 +388,15 @@ int64_t hfa_attn_fwd_workspace_size(hfa_dtype dtype, int64_t B, int64_t H, int64
   if ((dtype != HFA_F32 && dtype != HFA_BF16) || (d != 64 && d != 128)) return -1;
   if (B < 1 || H < 1 || N < 1 || B > INT64_MAX / H || N > INT_MAX / d || splits < 0) return -1;
   if (B * H > INT_MAX / N) return -1;
+  const bool library_choice = splits == 0;
   if (splits == 0) splits = auto_splits(dtype, B * H, N, d);
   if (dtype != HFA_BF16 && splits > 1) return -1;
+  if (dtype == HFA_F32) {
+    // 0: the library's choice (no workspace where packing would not pay);
+    // 1: the packed path's workspace in any case
+    if (library_choice && !f32_pack_pays(B * H, N, d)) return 0;
+    return f32_workspace_bytes(B * H, N, d);
+  }
   return split_workspace_bytes(make_split(N, d, splits).nsplit, B * H, N, d);
 }
 
@@ -356,12 +411,17 @@ hfa_status hfa_attn_fwd_split(const void* q, const void* k, const void* v, void*
   if (splits == 0) splits = auto_splits(dtype, BH, N, d);
   if (dtype != HFA_BF16 && splits > 1) return HFA_ERR_UNSUPPORTED;
   const KeySplit ks = make_split(N, d, splits);
-  if (ks.nsplit > 1) {
-    const int64_t need = split_workspace_bytes(ks.nsplit, BH, N, d);
+  // bf16: a workspace only for a split; fp32: optional, the packed path
+  // when one is given
+  const bool use_ws = dtype == HFA_F32 ? workspace != nullptr : ks.nsplit > 1;
+  if (use_ws) {
+    const int64_t need =
+        dtype == HFA_F32 ? f32_workspace_bytes(BH, N, d) : split_workspace_bytes(ks.nsplit, BH, N, d);
     if (!workspace) return HFA_ERR_NULL;
     if (misaligned(workspace, 16)) return HFA_ERR_ALIGN;
     if (workspace_bytes < need) return HFA_ERR_WORKSPACE;
-    const size_t bytes = static_cast<size_t>(BH) * static_cast<size_t>(N) * static_cast<size_t>(d) * 2;
+    const size_t elt = dtype == HFA_F32 ? 4 : 2;
+    const size_t bytes = static_cast<size_t>(BH) * static_cast<size_t>(N) * static_cast<size_t>(d) * elt;
     const size_t lse_bytes = static_cast<size_t>(BH) * static_cast<size_t>(N) * 4;
     const size_t wb = static_cast<size_t>(need);
     if (overlaps(workspace, wb, q, bytes) || overlaps(workspace, wb, k, bytes) || overlaps(workspace, wb, v, bytes) ||
@@ -370,7 +430,8 @@ hfa_status hfa_attn_fwd_split(const void* q, const void* k, const void* v, void*
   }
   const hfa_status dev = check_device();
   if (dev != HFA_OK) return dev;
-  return dispatch(q, k, v, o, lse, BH, N, d, scale, dtype, static_cast<hipStream_t>(stream), true, ks, workspace);
+  return dispatch(q, k, v, o, lse, BH, N, d, scale, dtype, static_cast<hipStream_t>(stream), true, ks,
+                  use_ws ? workspace : nullptr);
 }
 
 hfa_status hfa_attn_fwd_split_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -132,29 +132,48 @@ int64_t hfa_block_rows(hfa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t
  * always 1 for HFA_F32); 0 for invalid arguments.  No device, no HIP call. */
 int64_t hfa_key_splits(hfa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t d);
 
-/* Workspace bytes hfa_attn_fwd_split needs for `splits` ranges (0: the
- * automatic choice); 0 when the call splits nothing.  The requested count is
- * clamped to [1, min(ceil(N / 64), 32)] and every range is non-empty, so the
- * ranges actually used may be fewer.  -1 for invalid arguments (and for
- * splits > 1 with HFA_F32).  No device, no HIP call. */
+/* Workspace bytes of hfa_attn_fwd_split.
+ *
+ * HFA_BF16: the bytes `splits` key ranges need (0: the automatic choice); 0
+ * when the call splits nothing.  The requested count is clamped to
+ * [1, min(ceil(N / 64), 32)] and every range is non-empty, so the ranges
+ * actually used may be fewer.
+ *
+ * HFA_F32 (no key split; splits 0 or 1): the workspace of the packed path, in
+ * which a first kernel formats K and V once per call (the int8 slice planes
+ * and exponents of K, the bf16 pieces of V and per-tile key statistics,
+ * ceil(N / 64) tiles of 57344 bytes per head at d = 64, ceil(N / 32) tiles of
+ * 49152 bytes at d = 128) and the attention kernel copies those tiles into LDS
+ * as they are, instead of every workgroup formatting every key tile itself.
+ * Results are bit for bit those of hfa_attn_fwd.  splits == 0 asks for the
+ * library's choice: 0 bytes (no packing) where fewer than 8 workgroups of a
+ * head share each key tile, so that packing would not pay; splits == 1 gives
+ * the packed path's size in any case.
+ *
+ * -1 for invalid arguments (and for splits > 1 with HFA_F32).  No device, no
+ * HIP call. */
 int64_t hfa_attn_fwd_workspace_size(hfa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t d,
                                     int64_t splits);
 
-/* hfa_attn_fwd with an optional key split.
+/* hfa_attn_fwd with an optional key split (bf16) or packed K/V (fp32).
  *
  *   q ... dtype, stream  as for hfa_attn_fwd, validated the same way first.
  *   splits           key ranges per head: 0 = hfa_key_splits' choice, 1 = none
- *                    (the call is then exactly hfa_attn_fwd), > 1 bf16 only
+ *                    (a bf16 call is then exactly hfa_attn_fwd), > 1 bf16 only
  *                    (HFA_ERR_UNSUPPORTED for HFA_F32); < 0 is HFA_ERR_SHAPE.
  *   workspace        device memory of at least workspace_bytes >=
  *                    hfa_attn_fwd_workspace_size(dtype, B, H, N, d, splits)
  *                    bytes, 16-byte aligned, overlapping no other argument;
  *                    may be NULL when that size is 0.  Its contents on entry
- *                    do not matter; the call leaves the partial results there.
+ *                    do not matter; the call leaves the partial results
+ *                    (bf16) or the formatted tiles (fp32) there.  HFA_F32: a
+ *                    non-NULL workspace selects the packed path (it must then
+ *                    hold hfa_attn_fwd_workspace_size(..., 1) bytes); NULL
+ *                    runs hfa_attn_fwd.
  *
  * Errors, before any HIP call: those of hfa_attn_fwd, then HFA_ERR_NULL (no
  * workspace), HFA_ERR_ALIGN, HFA_ERR_WORKSPACE (too small), HFA_ERR_ALIAS.
- * Asynchronous on `stream` (two kernels in stream order); the library
+ * Asynchronous on `stream` (two kernels in stream order, or one); the library
  * allocates nothing.  Calls that share a workspace must not overlap in time. */
 hfa_status hfa_attn_fwd_split(const void* q, const void* k, const void* v, void* o, float* lse,
                               int64_t B, int64_t H, int64_t N, int64_t d, float scale, hfa_dtype dtype,
@@ -163,7 +182,8 @@ hfa_status hfa_attn_fwd_split(const void* q, const void* k, const void* v, void*
 /* hfa_attn_fwd_split for callers that cannot allocate device memory: code
  * under stream or graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  Same arguments and results as hfa_attn_fwd_split without the
- * workspace: the partial results go to a scratch array inside the library, of
+ * workspace (HFA_F32 calls take hfa_attn_fwd's path, which needs none): the
+ * partial results of a bf16 split go to a scratch array inside the library, of
  * 64 MiB, one per GPU (allocated when the library is loaded on that GPU and
  * held until the process ends); the call itself allocates nothing.  A split
  * whose workspace (hfa_attn_fwd_workspace_size) exceeds 64 MiB is rejected

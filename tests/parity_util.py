@@ -25,10 +25,28 @@ def _log(msg):
     print(msg, flush=True)
 
 
-def run_gpu(q, k, v, scale):
+def run_gpu(q, k, v, scale, splits=0):
+    """The Python entry point.  fp32 with splits=1: the packed path (a workspace
+    in which one kernel formats K and V once per call) whatever the shape."""
     dev = torch.device("cuda:0")
     qd, kd, vd = (t.to(dev) for t in (q, k, v))
-    o, lse = hfa.attn_fwd(qd, kd, vd, scale)
+    o, lse = hfa.attn_fwd(qd, kd, vd, scale, splits=splits)
+    torch.cuda.synchronize()
+    return o.float().cpu().double().numpy(), lse.cpu().double().numpy()
+
+
+def run_gpu_direct(q, k, v, scale):
+    """hfa_attn_fwd itself through the C ABI (fp32: every workgroup formats its
+    own K and V tiles, no workspace)."""
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (t.to(dev).contiguous() for t in (q, k, v))
+    B, H, N, d = qd.shape
+    o = torch.empty_like(qd)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    code = hfa.HFA_F32 if qd.dtype == torch.float32 else hfa.HFA_BF16
+    st = hfa.hfa_attn_fwd(qd.data_ptr(), kd.data_ptr(), vd.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, N, d,
+                          float(scale), code, torch.cuda.current_stream(dev).cuda_stream)
+    assert st == hfa.HFA_OK, hfa.hfa_status_str(st)
     torch.cuda.synchronize()
     return o.float().cpu().double().numpy(), lse.cpu().double().numpy()
 
@@ -61,9 +79,16 @@ def assert_close(name, got_o, got_lse, ref_o, ref_lse, dtype):
 
 
 def check_case(name, q, k, v, scale, dtype, rows=None):
+    """GPU against the oracle.  fp32 runs both paths, the packed one (Python
+    entry point, with a workspace) and hfa_attn_fwd without one: each meets the
+    tolerance, and the two agree bit for bit (the packing kernel leaves the same
+    bytes in LDS as the in-kernel formatting)."""
     _log(f"[parity] {name}")
-    go, gl = run_gpu(q, k, v, scale)
+    go, gl = run_gpu(q, k, v, scale, splits=1 if dtype == "f32" else 0)
     ro, rl = run_oracle(q, k, v, scale, rows)
+    if dtype == "f32":
+        do, dl = run_gpu_direct(q, k, v, scale)
+        assert np.array_equal(go, do) and np.array_equal(gl, dl), f"{name}: packed and direct fp32 paths differ"
     if rows is not None:
         go, gl = go[:, :, rows], gl[:, :, rows]
     assert_close(name, go, gl, ro, rl, dtype)

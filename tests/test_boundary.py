@@ -312,11 +312,46 @@ def test_split_validation_rejects_before_any_device_call(kw, status):
     assert _split_call(**kw) == status
 
 
+def test_f32_packed_workspace_size():
+    # fp32 has no key split; its workspace holds K and V formatted once per call:
+    # ceil(N/64) tiles of 57344 bytes per head at d=64 (K slice planes, exponents
+    # and statistics padded to 32 KiB, then the 24 KiB of V pieces), ceil(N/32)
+    # tiles of 49152 bytes at d=128.  splits=1 gives it in any case, splits=0 only
+    # where at least 8 workgroups of a head share each key tile.
+    assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_F32, 1, 1, 1000, 64, 1) == 16 * 57344
+    assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_F32, 2, 3, 100, 128, 1) == 6 * 4 * 49152
+    assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_F32, 1, 1, 1, 64, 1) == 57344
+    # B*H=32, N=2048, d=64: 256-row workgroups, 8 per head -> packs
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 4, 8, 2048, 64) == 256
+    assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_F32, 4, 8, 2048, 64, 0) == 32 * 32 * 57344
+    # B*H=32, N=1024: 128-row workgroups, 8 per head -> packs
+    assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_F32, 4, 8, 1024, 64, 0) == 32 * 16 * 57344
+    # B*H=256, N=200: one workgroup per head -> no packing
+    assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_F32, 1, 256, 200, 64, 0) == 0
+    # d=128 (128-row workgroups): N=1024 gives 8 per head, N=896 gives 7
+    assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_F32, 1, 4, 1024, 128, 0) == 4 * 32 * 49152
+    assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_F32, 1, 4, 896, 128, 0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(workspace=WS + 8), hfa.HFA_ERR_ALIGN),
+    (dict(workspace_bytes=2 * 16 * 57344 - 1), hfa.HFA_ERR_WORKSPACE),
+    (dict(workspace=GOOD["k"] + 4096), hfa.HFA_ERR_ALIAS),      # overlaps k
+    (dict(workspace=GOOD["o"] - 2 * 16 * 57344 + 16), hfa.HFA_ERR_ALIAS),  # ends inside o
+])
+def test_f32_packed_validation(kw, status):
+    # B=1 H=2 N=1000 d=64 fp32: 2 x 16 tiles of 57344 bytes
+    assert _split_call(splits=1, dtype=hfa.HFA_F32, d=64, **kw) == status
+
+
 def test_split_one_needs_no_workspace():
     if torch.cuda.is_available():
         pytest.skip("would launch on a visible GPU with fake pointers")
     assert _split_call(splits=1, workspace=None, workspace_bytes=0) == hfa.HFA_ERR_NO_DEVICE
     assert _split_call(splits=4, workspace_bytes=4 * 2 * 1000 * 129 * 4) == hfa.HFA_ERR_NO_DEVICE
+    # fp32: no workspace runs hfa_attn_fwd's path, one of the packed size the packed path
+    assert _split_call(splits=1, dtype=hfa.HFA_F32, d=64, workspace=None, workspace_bytes=0) == hfa.HFA_ERR_NO_DEVICE
+    assert _split_call(splits=0, dtype=hfa.HFA_F32, d=64, workspace_bytes=2 * 16 * 57344) == hfa.HFA_ERR_NO_DEVICE
 
 
 def test_noalloc_rejects_before_any_device_call():

@@ -22,7 +22,7 @@ import oracle
 from fa2_fwd_amd import workloads as W
 
 from parity_util import (BF16_ATOL, BF16_RTOL, F32_ATOL, _log, assert_close, check_case, f32_tolerance,  # noqa: F401
-                         run_gpu, run_oracle)
+                         run_gpu, run_gpu_direct, run_oracle)
 
 pytestmark = pytest.mark.gpu
 
@@ -437,3 +437,39 @@ def test_split_with_caller_workspace_and_repeat():
     torch.cuda.synchronize()
     assert (o1.float() - o3.float()).abs().max().item() <= 2e-2
     assert (l1 - l3).abs().max().item() <= 1e-3
+
+
+# ---- fp32 packed K/V (hfa_attn_fwd_split with a workspace) -----------------
+
+def test_f32_packed_workspace_reuse():
+    # One workspace, filled with junk, then used by a larger call and a smaller
+    # one of another head dim (leftover tiles of the first stay behind it): each
+    # call equals hfa_attn_fwd bit for bit, and the oracle.
+    dev = torch.device("cuda:0")
+    need = hfa.hfa_attn_fwd_workspace_size(hfa.HFA_F32, 2, 8, 1500, 64, 1)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=dev)
+    for (B, H, N, d, seed) in [(2, 8, 1500, 64, 8200), (1, 3, 333, 128, 8201), (1, 1, 70, 64, 8202)]:
+        assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_F32, B, H, N, d, 1) <= need
+        q, k, v = W.make_inputs(B, H, N, d, "f32", seed=seed, qk_mult=2.0)
+        qd, kd, vd = (t.to(dev) for t in (q, k, v))
+        o1, l1 = hfa.attn_fwd(qd, kd, vd, splits=1, workspace=ws)
+        torch.cuda.synchronize()
+        do, dl = run_gpu_direct(q, k, v, 1.0 / math.sqrt(d))
+        go, gl = o1.cpu().double().numpy(), l1.cpu().double().numpy()
+        assert np.array_equal(go, do) and np.array_equal(gl, dl), (B, H, N, d)
+        rows = W.sample_rows(N, 24, seed=seed)
+        ro, rl = run_oracle(q, k, v, 1.0 / math.sqrt(d), rows)
+        assert_close(f"f32 packed reuse B={B} H={H} N={N} d={d}", go[:, :, rows], gl[:, :, rows], ro, rl, "f32")
+
+
+def test_f32_default_call_packs_where_it_pays():
+    # The Python entry point's default takes the library's choice: a workspace
+    # (packed path) for B*H=32 N=2048 d=64, none for B*H=256 N=200; both give
+    # hfa_attn_fwd's bits.
+    for (B, H, N, seed) in [(4, 8, 2048, 8300), (1, 256, 200, 8301)]:
+        q, k, v = W.make_inputs(B, H, N, 64, "f32", seed=seed)
+        packs = hfa.hfa_attn_fwd_workspace_size(hfa.HFA_F32, B, H, N, 64, 0) > 0
+        assert packs == (N == 2048)
+        go, gl = run_gpu(q, k, v, 0.125)
+        do, dl = run_gpu_direct(q, k, v, 0.125)
+        assert np.array_equal(go, do) and np.array_equal(gl, dl)
