@@ -717,11 +717,31 @@ def summarize_trace(n: int, trace_dir: str, trace_json: str, bench_json: str | N
              f"| the traced run's own event timing (`ms_per_step` of its JSON line) | {traced_ms:.5f} |"]
     if bench_ms is not None:
         lines.append(f"| unprofiled `python bench.py` in the same job (`ms_per_step` of this workload) | {bench_ms:.5f} |")
+    # other kernels of each step (the fp32 packing kernel, the bf16 key-split merge)
+    others = {}
+    for r in _csv_rows(trace_dir, "kernel_trace.csv"):
+        name = r["Kernel_Name"]
+        if "attn_fwd" not in name and ("f32_pack_kernel" in name or "attn_merge" in name):
+            others.setdefault(name, []).append(r)
+    step_total = avg_timed
+    for name, rs in sorted(others.items()):
+        rs.sort(key=lambda r: int(r["Dispatch_Id"]))
+        od = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rs][-steps:]
+        avg_o = sum(od) / len(od)
+        step_total += avg_o
+        lines.append(f"| trace: average of the last {len(od)} dispatches of `{name.split('(')[0][:80]}` (same step) "
+                     f"| {avg_o / 1e6:.5f} |")
+    if others:
+        lines.append(f"| trace: the step's kernels together | {step_total / 1e6:.5f} |")
     lines += ["",
               f"From the trace: {tflops_trace:.1f} TFLOP/s = {frac_trace:.4f} of the {roof['peak']} TFLOP/s "
               f"roofline (the line: {roof['achieved']} TFLOP/s, frac {roof['frac']}).",
               f"Trace average / event ms_per_step of the traced run: {avg_timed / 1e6 / traced_ms:.4f}"
               + (f"; / unprofiled ms_per_step: {avg_timed / 1e6 / bench_ms:.4f}." if bench_ms else "."), ""]
+    if others:
+        lines += [f"The step also runs the kernels listed after the attention kernel; all of them together: "
+                  f"{step_total / 1e6 / traced_ms:.4f} of the traced run's ms_per_step"
+                  + (f", {step_total / 1e6 / bench_ms:.4f} of the unprofiled one." if bench_ms else "."), ""]
     if traffic is not None:
         t = traffic
         lines += ["## HBM bytes (rocprofv3 --pmc, one counter per run)", "",

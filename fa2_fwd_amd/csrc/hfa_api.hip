@@ -276,11 +276,15 @@ hfa_status dispatch(const void* q, const void* k, const void* v, void* o, float*
   return launch_f32<F32D128>(q, k, v, o, lse, BH, N, scale, st, launch, work);
 }
 
-// Formatting K and V once per call pays when at least this many query-row
-// tiles (workgroups) of a head share each key tile: each of them would
-// otherwise format every key tile itself.  Measured break-even on MI355X at
-// about 8 (B*H=32, N=2048 and N=1024, d=64).
+// Formatting K and V once per call pays when enough query-row tiles
+// (workgroups) of a head share each key tile, each of which would otherwise
+// format every key tile itself, and when the heads are long enough for the
+// attention work (N^2 per head) to hide the packing pass (N per head).
+// Measured on MI355X at d=64: +1-3 % at N=2048 (8 row tiles), +4 % at 4096,
+// +7 % at 16384, break-even at N=1024, -23 % at N=200 (one row tile); at
+// d=128: +12 % at N=2048, +26 % at 4096.
 constexpr int64_t kPackMinRowTiles = 8;
+constexpr int64_t kPackMinKeyTiles = 32;
 
 // The fp32 tiling's query rows per workgroup.
 int64_t f32_block_rows(int64_t BH, int64_t N, int64_t d) {
@@ -291,7 +295,8 @@ int64_t f32_block_rows(int64_t BH, int64_t N, int64_t d) {
 
 bool f32_pack_pays(int64_t BH, int64_t N, int64_t d) {
   const int64_t br = f32_block_rows(BH, N, d);
-  return (N + br - 1) / br >= kPackMinRowTiles;
+  const int64_t kt = d == 128 ? F32D128::KT : F32D64Big::KT;
+  return (N + br - 1) / br >= kPackMinRowTiles && (N + kt - 1) / kt >= kPackMinKeyTiles;
 }
 
 // Workspace bytes of the packed fp32 path for the tiling the call would use.

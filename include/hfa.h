@@ -146,9 +146,10 @@ int64_t hfa_key_splits(hfa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t
  * 49152 bytes at d = 128) and the attention kernel copies those tiles into LDS
  * as they are, instead of every workgroup formatting every key tile itself.
  * Results are bit for bit those of hfa_attn_fwd.  splits == 0 asks for the
- * library's choice: 0 bytes (no packing) where fewer than 8 workgroups of a
- * head share each key tile, so that packing would not pay; splits == 1 gives
- * the packed path's size in any case.
+ * library's choice: the workspace where at least 8 workgroups of a head share
+ * each key tile and a head has at least 32 key tiles, 0 bytes (no packing)
+ * elsewhere, where the packing pass would not pay for itself; splits == 1
+ * gives the packed path's size in any case.
  *
  * -1 for invalid arguments (and for splits > 1 with HFA_F32).  No device, no
  * HIP call. */

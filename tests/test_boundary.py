@@ -324,11 +324,14 @@ def test_f32_packed_workspace_size():
     # B*H=32, N=2048, d=64: 256-row workgroups, 8 per head -> packs
     assert hfa.hfa_block_rows(hfa.HFA_F32, 4, 8, 2048, 64) == 256
     assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_F32, 4, 8, 2048, 64, 0) == 32 * 32 * 57344
-    # B*H=32, N=1024: 128-row workgroups, 8 per head -> packs
-    assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_F32, 4, 8, 1024, 64, 0) == 32 * 16 * 57344
+    # B*H=32, N=1024: 128-row workgroups, 8 per head, but only 16 key tiles -> no packing
+    assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_F32, 4, 8, 1024, 64, 0) == 0
     # B*H=256, N=200: one workgroup per head -> no packing
     assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_F32, 1, 256, 200, 64, 0) == 0
-    # d=128 (128-row workgroups): N=1024 gives 8 per head, N=896 gives 7
+    # B*H=1024, N=4096: 256-row workgroups, 16 per head, 64 key tiles -> packs
+    assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_F32, 4, 256, 4096, 64, 0) == 1024 * 64 * 57344
+    # d=128 (128-row workgroups, 32-key tiles): N=1024 gives 8 per head and 32 key
+    # tiles, N=896 gives 7
     assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_F32, 1, 4, 1024, 128, 0) == 4 * 32 * 49152
     assert hfa.hfa_attn_fwd_workspace_size(hfa.HFA_F32, 1, 4, 896, 128, 0) == 0
 
