@@ -15,9 +15,10 @@
 //  * Resident path (cols <= NT * 4 * ITEMS): the thread's elements stay in
 //    registers between the reduction and the output: x is read once, with
 //    non-temporal loads.
-//  * Streaming path: the thread's running pair is updated chunk by chunk
-//    while x streams through (UNROLL 16-byte loads in flight per thread), then
-//    x is read a second time, last chunk first, to write y.
+//  * Wide path: the first part of the row stays on chip between the passes
+//    (registers, then LDS: about half of the on-chip space of a CU), the rest
+//    updates the running pair chunk by chunk as it streams through and is read
+//    a second time, last chunk first, to write y.
 //
 // y is written with non-temporal stores.  Exponentials are exp2 of
 // (x - M) * log2(e), the difference taken first so that large |x| loses no
@@ -148,30 +149,115 @@ __global__ __launch_bounds__(NT) void softmax_rows_resident_kernel(const float* 
   store_slots<NT, VEC, ITEMS>(yr, 0, cols, tid, v, p.m, 1.0f / p.l);
 }
 
-// Streaming path: x read twice, UNROLL slots per thread in flight.
-template <int NT, int UNROLL, bool VEC>
-__global__ __launch_bounds__(NT) void softmax_rows_stream_kernel(const float* x, float* y, int64_t cols) {
+// Slots of the wide kernel, addressed as a wave-uniform base (the row, plus
+// the slot's offset) and one 32-bit lane offset shared by every slot, so that
+// no per-slot address is held in vector registers.  VEC: slot s of thread t is
+// the 16 bytes at element (s NT + t) 4 of the row; else element e of it is
+// element (4 s + e) NT + t.  lane4 = 4 t.  Elements past the row read as -inf.
+template <int NT, bool VEC, int N, bool NT_LOAD>
+__device__ __forceinline__ void wide_load(const float* xr, int64_t s0, int64_t cols, uint32_t lane4,
+                                          float (&v)[N * 4]) {
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const int64_t slot0 = (s0 + u) * NT * 4;  // first element of the slot
+    if (VEC) {
+      const float* base = xr + slot0;
+      f32x4 q = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      if (static_cast<int64_t>(lane4) < cols - slot0)
+        q = load16<NT_LOAD>(reinterpret_cast<const f32x4*>(reinterpret_cast<const char*>(base) + 4 * lane4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * u + e] = q[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float* base = xr + slot0 + e * NT;
+        v[4 * u + e] = static_cast<int64_t>(lane4 / 4) < cols - slot0 - e * NT
+                           ? *reinterpret_cast<const float*>(reinterpret_cast<const char*>(base) + lane4)
+                           : -INFINITY;
+      }
+    }
+  }
+}
+
+template <int NT, bool VEC, int N>
+__device__ __forceinline__ void wide_store(float* yr, int64_t s0, int64_t cols, uint32_t lane4, const float (&v)[N * 4],
+                                           float M, float inv) {
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const int64_t slot0 = (s0 + u) * NT * 4;
+    float o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = exp2_hw((v[4 * u + e] - M) * kLog2eF) * inv;
+    if (VEC) {
+      if (static_cast<int64_t>(lane4) < cols - slot0)
+        store16<true>(reinterpret_cast<f32x4*>(reinterpret_cast<char*>(yr + slot0) + 4 * lane4),
+                      f32x4{o[0], o[1], o[2], o[3]});
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (static_cast<int64_t>(lane4 / 4) < cols - slot0 - e * NT)
+          *reinterpret_cast<float*>(reinterpret_cast<char*>(yr + slot0 + e * NT) + lane4) = o[e];
+    }
+  }
+}
+
+// Wide rows: the first RS slots of every thread stay in registers and the next
+// LS slots in LDS (dynamic, LS * NT * 16 bytes) between the two passes; only
+// the slots after them are read a second time, last first (the likeliest to be
+// in the caches).  Loads in flight per thread: all RS at once, then UL per
+// step over the LDS slots and US per step over the rest.
+template <int NT, int RS, int LS, int UL, int US, bool VEC>
+__global__ __launch_bounds__(NT) void softmax_rows_wide_kernel(const float* x, float* y, int64_t cols) {
+  static_assert(LS % UL == 0, "the LDS slots are read in whole steps");
   __shared__ SoftmaxPair lds[NT / 64];
+  extern __shared__ f32x4 held[];  // [LS][NT]
   const int tid = thread_id();
-  const int64_t row = group_id();
+  const int64_t row = uniform_sgpr(group_id());
   const float* xr = x + row * cols;
   float* yr = y + row * cols;
-  constexpr int64_t STEP = static_cast<int64_t>(NT) * 4 * UNROLL;
-  SoftmaxPair p = {-INFINITY, 0.0f};
-  for (int64_t base = 0; base < cols; base += STEP) {
-    float v[UNROLL * 4];
-    load_slots<NT, VEC, UNROLL, false>(xr, base, cols, tid, v);
+  // 4 tid: the lane's first element within a slot (VEC; its byte offset is
+  // 16 tid), or the byte offset of its element within each quarter (scalar)
+  const uint32_t lane4 = 4u * static_cast<uint32_t>(tid);
+  constexpr int64_t SLOT = static_cast<int64_t>(NT) * 4;
+  const int64_t nslots = (cols + SLOT - 1) / SLOT;
+  float r[RS * 4];
+  wide_load<NT, VEC, RS, true>(xr, 0, cols, lane4, r);
+  SoftmaxPair p = fold_values(SoftmaxPair{-INFINITY, 0.0f}, r);
+  const int lsteps = static_cast<int>(nslots > RS ? min<int64_t>((nslots - RS + UL - 1) / UL, LS / UL) : 0);
+  for (int st = 0; st < lsteps; ++st) {
+    float v[UL * 4];
+    wide_load<NT, VEC, UL, true>(xr, RS + st * UL, cols, lane4, v);
+    p = fold_values(p, v);
+#pragma unroll
+    for (int u = 0; u < UL; ++u)
+      held[(st * UL + u) * NT + tid] = f32x4{v[4 * u], v[4 * u + 1], v[4 * u + 2], v[4 * u + 3]};
+  }
+  constexpr int64_t KEPT = RS + LS;  // slots held on chip
+  for (int64_t s = KEPT; s < nslots; s += US) {
+    float v[US * 4];
+    wide_load<NT, VEC, US, false>(xr, s, cols, lane4, v);
     p = fold_values(p, v);
   }
   p = merge_workgroup<NT>(p, lds);
   const float inv = 1.0f / p.l;
-  // The second pass walks the row backwards: the chunks read last by the
-  // first pass are the likeliest still to be held by the caches.
-  for (int64_t base = (cols - 1) / STEP * STEP; base >= 0; base -= STEP) {
-    float v[UNROLL * 4];
-    load_slots<NT, VEC, UNROLL, false>(xr, base, cols, tid, v);
-    store_slots<NT, VEC, UNROLL>(yr, base, cols, tid, v, p.m, inv);
+  if (nslots > KEPT) {
+    for (int64_t s = KEPT + (nslots - 1 - KEPT) / US * US; s >= KEPT; s -= US) {
+      float v[US * 4];
+      wide_load<NT, VEC, US, false>(xr, s, cols, lane4, v);
+      wide_store<NT, VEC, US>(yr, s, cols, lane4, v, p.m, inv);
+    }
   }
+  for (int st = 0; st < lsteps; ++st) {
+    float v[UL * 4];
+#pragma unroll
+    for (int u = 0; u < UL; ++u) {
+      const f32x4 h = held[(st * UL + u) * NT + tid];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * u + e] = h[e];
+    }
+    wide_store<NT, VEC, UL>(yr, RS + st * UL, cols, lane4, v, p.m, inv);
+  }
+  wide_store<NT, VEC, RS>(yr, 0, cols, lane4, r, p.m, inv);
 }
 
 }  // namespace hfa

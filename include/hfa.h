@@ -232,11 +232,13 @@ void hfa_graph_destroy(hfa_graph g);
  *
  * The stable row softmax of the book chapter "Triton and kernel fusion"
  * (section "Fusion": one read of x and one write of y), for any row width:
- * rows wider than one workgroup holds in registers (more than 32768 columns)
- * take the route of that chapter's stretch exercise, a running max and running
- * sum per thread (the online normalisation identity of neuralmasteryai
- * "Hardware Acceleration & Custom Kernels", section 2, step 2), and read x a
- * second time to write y.  Arithmetic is fp32 with hardware exp2.
+ * rows wider than one workgroup holds in registers (more than 65536 columns,
+ * 49152 without 16-byte alignment) take the route of that chapter's stretch
+ * exercise, a running max and running sum per thread (the online
+ * normalisation identity of neuralmasteryai "Hardware Acceleration & Custom
+ * Kernels", section 2, step 2); their first 143360 (139264) columns stay on
+ * chip between the two passes and the rest of x is read a second time to write
+ * y.  Arithmetic is fp32 with hardware exp2.
  *
  *   x, y        device, [rows, cols] contiguous fp32, 4-byte aligned (16-byte
  *               alignment with cols % 4 == 0 takes 16-byte accesses).  y may

@@ -67,7 +67,7 @@ def test_softmax_and_rmsnorm_under_torch_graph_capture():
     # eager result, with unrelated eager work and fills between replays.
     dev = torch.device("cuda:0")
     g = torch.Generator("cpu").manual_seed(21)
-    xs = (torch.randn(64, 70001, generator=g) * 4.0).to(dev)  # streaming softmax path, ragged width
+    xs = (torch.randn(64, 70001, generator=g) * 4.0).to(dev)  # wide softmax path (element-wise layout), ragged width
     xs2 = (torch.randn(128, 3000, generator=g) * 4.0).to(dev)  # register-resident path
     rw = W.RmsNormWorkload("graph", 300, 4096, "bf16", 22)
     xr, rr, wr = (t.to(dev) for t in rw.inputs())

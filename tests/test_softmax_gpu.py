@@ -2,10 +2,11 @@
 
 Tolerance: max |gpu - oracle| <= 1e-5 per element (the fp32 bound used for
 attention; softmax outputs lie in [0, 1]).  Shapes cover the book chapter's
-[4096, 32000] matrix, rows wider than its one-block limit (65536, the
-streaming path), widths that are not multiples of 4 and misaligned rows (the
-scalar path), tiny widths, in-place use, inputs near the exp overflow range and
--inf entries.
+[4096, 32000] matrix, rows wider than its one-block limit (65536: up to 65536
+columns in registers, wider rows partly on chip and partly read twice), widths
+that are not multiples of 4 and misaligned rows (the element-wise layout),
+tiny widths, in-place use, inputs near the exp overflow range and -inf
+entries.
 """
 
 import numpy as np
@@ -96,10 +97,16 @@ def test_softmax_rows_rows_sum_to_one_on_device():
     assert torch.all((s - 1).abs() < 1e-4)
 
 
-# Rows wider than the register-resident limit (32768 columns) with 16-byte
-# accesses: the streaming kernel, at widths around chunk boundaries and far past them.
-WIDE = [(3, 32772), (2, 72700), (2, 72704), (2, 90000), (2, 105472), (2, 138236), (2, 138240), (2, 156668),
-        (2, 156672), (2, 156676), (2, 300000), (1, 1 << 20)]
+# Rows around and past the register-resident limits (49152 and 65536 columns:
+# 24 and 32 slots of 2048 columns) with 16-byte accesses, then the wide
+# kernel, whose first 52 slots of 2048 columns stay in
+# registers (106496 columns), the next 18 in LDS, filled 6 slots per step
+# (to 143360), the rest read twice in steps of 8 slots; widths around each of
+# those boundaries and far past them.
+WIDE = [(3, 32772), (2, 49148), (2, 49152), (2, 49156), (2, 65532), (2, 65536), (2, 65540), (2, 72700),
+        (2, 72704), (2, 90000), (2, 102400), (2, 106492), (2, 106496), (2, 106500),
+        (2, 118784), (2, 118788), (2, 131076), (2, 138236), (2, 143356), (2, 143360), (2, 143364), (2, 156668),
+        (2, 156672), (2, 176128), (2, 176132), (2, 300000), (1, 1 << 20)]
 
 
 @pytest.mark.parametrize("rows,cols", WIDE)
@@ -142,7 +149,7 @@ def test_softmax_rows_wide_large_magnitudes_and_minus_inf():
 
 @pytest.mark.parametrize("rows,cols", [(4096, 32000), (256, 262144), (64, 70001)])
 def test_softmax_rows_bitwise_repeatable(rows, cols):
-    # the resident and the streaming kernel (block reductions through LDS): three runs agree bit for bit
+    # the resident and the wide kernel (block reductions through LDS): three runs agree bit for bit
     dev = torch.device("cuda:0")
     x = _x(rows, cols, seed=rows + cols).to(dev)
     y0 = hfa.softmax_rows(x)
@@ -150,3 +157,15 @@ def test_softmax_rows_bitwise_repeatable(rows, cols):
         y = hfa.softmax_rows(x)
         torch.cuda.synchronize()
         assert torch.equal(y, y0)
+
+
+@pytest.mark.parametrize("cols", [32767, 49151, 49153, 102401, 139265, 200003])
+def test_softmax_rows_wide_unaligned(cols):
+    # widths that are not a multiple of 4: the element-wise layout, resident up to
+    # 24 slots (49152 columns), then the wide kernel (50 register slots, to 102400;
+    # LDS to 139264), with the register, LDS and twice-read parts all in use at 200003
+    x = _x(2, cols, seed=cols + 7)
+    y = hfa.softmax_rows(x.cuda())
+    torch.cuda.synchronize()
+    _check(f"wide unaligned 2x{cols}", x, y)
+
