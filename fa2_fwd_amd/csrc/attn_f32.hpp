@@ -41,6 +41,12 @@
 //  * The running denominator is accumulated in fp64, and the log-sum-exp is
 //    combined in fp64 and rounded once.
 //
+// K/V staging, two routes with the same LDS image and therefore the same
+// bits: every workgroup formats each key tile itself as it stages it (slices
+// and exponents of K, pieces of V), or, given a workspace, f32_pack_kernel
+// formats every tile once per call and the attention kernel copies the tile
+// images from HBM into LDS as they are (global_load_lds_dwordx4).
+//
 // Matrix-core mapping.  S^T on v_mfma_i32_16x16x64_i8: A = one slice of 16
 // key rows (64 head-dim columns per instruction, lane group g holding columns
 // 16g .. 16g + 15), B = one slice of 16 query rows in the same column order;
