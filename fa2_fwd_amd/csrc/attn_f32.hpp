@@ -816,6 +816,10 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_f32_kernel(
               if (key0 + kb * 16 + 4 * g + r >= N) s[qb][kb][r] = -INFINITY;
         }
         softmax_block_f32<T>(s[qb], p[qb], m2[qb], l_run[qb], acc[qb], c2);
+        // The next block reads the K slices from LDS again: without this the
+        // compiler keeps every 16-key block's slices in registers from the
+        // first block to the second, and the tile spills.
+        if (qb + 1 < QB) asm volatile("" ::: "memory");
       }
     } else {
 #pragma unroll
