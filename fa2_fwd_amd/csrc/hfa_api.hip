@@ -52,8 +52,13 @@ using namespace hfa::api;
 #ifndef HFA_F32_D64_TINY_TILE
 #define HFA_F32_D64_TINY_TILE 1, 4, 64
 #endif
+// fp32, d = 128: 128-row workgroups (one block per wave, 8 waves), and
+// 64-row ones (4 waves) for shapes whose 128-row grid leaves CUs idle.
 #ifndef HFA_F32_D128_TILE
 #define HFA_F32_D128_TILE 1, 8, 32
+#endif
+#ifndef HFA_F32_D128_TINY_TILE
+#define HFA_F32_D128_TINY_TILE 1, 4, 32
 #endif
 using Bf16D128 = Bf16Tile<128, HFA_BF16_D128_TILE>;
 using Bf16D64 = Bf16Tile<64, HFA_BF16_D64_TILE>;
@@ -64,6 +69,9 @@ using F32D64Big = F32Tile<64, HFA_F32_D64_BIG_TILE>;
 using F32D64Small = F32Tile<64, HFA_F32_D64_SMALL_TILE>;
 using F32D64Tiny = F32Tile<64, HFA_F32_D64_TINY_TILE>;
 using F32D128 = F32Tile<128, HFA_F32_D128_TILE>;
+using F32D128Tiny = F32Tile<128, HFA_F32_D128_TINY_TILE>;
+static_assert(F32D128Tiny::PACKB == F32D128::PACKB && F32D128Tiny::KT == F32D128::KT,
+              "both d = 128 tilings use the same packed tile images");
 
 constexpr double kLog2e = 1.44269504088896340736;  // 1 / ln 2
 constexpr int64_t kComputeUnits = 256;  // gfx950 (MI350 series): 8 XCDs x 32 CUs
@@ -273,7 +281,8 @@ hfa_status dispatch(const void* q, const void* k, const void* v, void* o, float*
       default: return launch_f32<F32D64Tiny>(q, k, v, o, lse, BH, N, scale, st, launch, work);
     }
   }
-  return launch_f32<F32D128>(q, k, v, o, lse, BH, N, scale, st, launch, work);
+  if (fills_cus(BH, N, F32D128::BR)) return launch_f32<F32D128>(q, k, v, o, lse, BH, N, scale, st, launch, work);
+  return launch_f32<F32D128Tiny>(q, k, v, o, lse, BH, N, scale, st, launch, work);
 }
 
 // Formatting K and V once per call pays when enough query-row tiles
@@ -288,7 +297,7 @@ constexpr int64_t kPackMinKeyTiles = 32;
 
 // The fp32 tiling's query rows per workgroup.
 int64_t f32_block_rows(int64_t BH, int64_t N, int64_t d) {
-  if (d == 128) return F32D128::BR;
+  if (d == 128) return fills_cus(BH, N, F32D128::BR) ? F32D128::BR : F32D128Tiny::BR;
   const int t = f32_d64_tiling(BH, N);
   return t == 2 ? F32D64Big::BR : t == 1 ? F32D64Small::BR : F32D64Tiny::BR;
 }
@@ -352,7 +361,7 @@ int64_t hfa_block_rows(hfa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t
     const int t = f32_d64_tiling(B * H, N);
     return t == 2 ? F32D64Big::BR : t == 1 ? F32D64Small::BR : F32D64Tiny::BR;
   }
-  if (dtype == HFA_F32 && d == 128) return F32D128::BR;
+  if (dtype == HFA_F32 && d == 128) return fills_cus(B * H, N, F32D128::BR) ? F32D128::BR : F32D128Tiny::BR;
   return 0;
 }
 

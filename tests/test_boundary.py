@@ -86,6 +86,13 @@ def test_block_rows_follow_the_shape():
     assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 255, 256, 64) == 128
     assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 16, 1024, 64) == 64
     assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 8, 4096, 64) == 128
+    # fp32 d=128 has two tilings: 128 rows when B*H*ceil(N/128) >= 256, else 64.
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 2, 8, 2048, 128) == 128
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 16, 2048, 128) == 128
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 16, 1024, 128) == 64
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 4, 4096, 128) == 64
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 255, 128, 128) == 64
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 256, 100, 128) == 128
 
 
 @pytest.mark.parametrize("kw,status", [

@@ -203,6 +203,18 @@ def test_f32_d64_all_tilings(B, H, N):
     check_case(f"f32 d=64 B={B} H={H} N={N} (B_r={br})", q, k, v, 0.125, "f32", rows=rows)
 
 
+@pytest.mark.parametrize("B,H,N", [(1, 4, 4096), (1, 16, 1024), (2, 2, 1500), (1, 1, 33), (2, 8, 2048),
+                                   (1, 16, 2047)])
+def test_f32_d128_both_tilings(B, H, N):
+    # fp32 d=128 takes 128-row workgroups when B*H*ceil(N/128) >= 256, else 64-row
+    # ones (4 waves); both, ragged N (check_case runs the packed path too).
+    br = hfa.hfa_block_rows(hfa.HFA_F32, B, H, N, 128)
+    assert br == (128 if B * H * -(-N // 128) >= 256 else 64)
+    q, k, v = W.make_inputs(B, H, N, 128, "f32", seed=B * 1000 + H + N + 128, qk_mult=2.0)
+    rows = W.sample_rows(N, 24, seed=N)
+    check_case(f"f32 d=128 B={B} H={H} N={N} (B_r={br})", q, k, v, 1.0 / math.sqrt(128), "f32", rows=rows)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("d", [64, 128])
 def test_rising_scores(dtype, d):
