@@ -341,13 +341,20 @@ __device__ __forceinline__ void exact_rows_impl(const float* __restrict__ Qh, co
 
 // ---- S^T = K Q^T from the int8 slices for one 16-key block (slices ks of
 // the block's key rows, ek their exponents) and one 16-query block (slices
-// qsb, exponent eqb): the slice products with a + b = t accumulate exactly in
-// acc_t (|acc_t| < 2^21), then s = 2^(eq + ek - 12) sum_t acc_t 2^(-7t) in
-// fp64, combined as 2^-35 (acc01 2^28 + acc23 2^14 + acc45) with
-// acc01 = 2^7 acc_0 + acc_1 etc. formed exactly in int32.
+// qsb): the slice products with a + b = t accumulate exactly in acc_t
+// (|acc_t| < 2^21), and s = 2^(eq + ek - 12) sum_t acc_t 2^(-7t) is
+// 2^(eq - 47) 2^ek (acc01 2^28 + acc23 2^14 + acc45) with acc01 = 2^7 acc_0 +
+// acc_1 etc. formed exactly in int32.  This returns s 2^(47 - eq) 2^e_add,
+// exact in fp64 up to the one rounding of the sum.  The query's factor
+// 2^(eq - 47) is the same for all its keys, so it can go into c2 instead
+// (e_add = 0, and c2q below), saving an add per score.  The d = 64 tiles do
+// that except the unpacked 256-row one, where the per-query-block c2q would
+// not fit in its registers; the d = 128 tiles keep the factor here
+// (e_add = eq - 47): folded, their packed 64-row tile ran 8 % slower.  Either
+// way the products with c2 are the same bits.
 template <class T>
 __device__ __forceinline__ f64x4 score_block_f32(const i32x4 (&ks)[T::D / 64][T::NSL],
-                                                 const u32x4 (&qsb)[T::D / 64][T::NSL], i32x4 ek, int eqb) {
+                                                 const u32x4 (&qsb)[T::D / 64][T::NSL], i32x4 ek, int e_add) {
   i32x4 at[2 * T::NSL - 4];
 #pragma unroll
   for (int t = 0; t < 2 * T::NSL - 4; ++t) at[t] = i32x4{0, 0, 0, 0};
@@ -368,17 +375,20 @@ __device__ __forceinline__ f64x4 score_block_f32(const i32x4 (&ks)[T::D / 64][T:
     const int a45 = at[4][r] * 128 + at[5][r];
     const double x = fma(static_cast<double>(a01), 268435456.0,
                          fma(static_cast<double>(a23), 16384.0, static_cast<double>(a45)));
-    s[r] = __builtin_amdgcn_ldexp(x, eqb + ek[r] - 47);
+    s[r] = __builtin_amdgcn_ldexp(x, ek[r] + e_add);
   }
   return s;
 }
 
 // ---- online softmax update of one 16-query block over a key tile: scores
-// sb, weights pb out; running max m2 (log2 units), denominator l and output
-// sums accb updated.
+// sb (the true scores times a power of two, see score_block_f32), weights pb
+// out; running max m2 (log2 units), denominator l and output sums accb
+// updated.  c2q is |scale| log2(e) times the inverse power of two, so sb c2q
+// is the score in log2 units: power-of-two factors being exact, the products
+// equal those of the true scores with |scale| log2(e).
 template <class T>
 __device__ __forceinline__ void softmax_block_f32(const f64x4 (&sb)[T::KT / 16], f32x4 (&pb)[T::KT / 16], double& m2,
-                                                  double& l, f32x4 (&accb)[T::D / 16], double c2) {
+                                                  double& l, f32x4 (&accb)[T::D / 16], double c2q) {
   double mx = -INFINITY;
 #pragma unroll
   for (int kb = 0; kb < T::KT / 16; ++kb)
@@ -387,14 +397,14 @@ __device__ __forceinline__ void softmax_block_f32(const f64x4 (&sb)[T::KT / 16],
   mx = max_xor<16>(mx);
   mx = max_xor<32>(mx);
   // log2-domain running max, rounded up to an integer: exact rescale factors.
-  const double m_new = fmax(m2, ceil(mx * c2));
+  const double m_new = fmax(m2, ceil(mx * c2q));
   const float alpha = exp2_hw(static_cast<float>(m2 - m_new));  // 0 on the first tile
   float ts = 0.0f;
 #pragma unroll
   for (int kb = 0; kb < T::KT / 16; ++kb)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float x = exp2_hw(static_cast<float>(fma(sb[kb][r], c2, -m_new)));
+      const float x = exp2_hw(static_cast<float>(fma(sb[kb][r], c2q, -m_new)));
       pb[kb][r] = x;
       ts += x;
     }
@@ -559,6 +569,10 @@ void attn_fwd_f32_kernel(
   const float qmul = static_cast<float>(q_mode);
   u32x4 qs[QB][D / 64][T::NSL];
   int eq[QB];
+  // Where the query exponent goes (see score_block_f32): c2q[qb] =
+  // 2^(eq - 47) c2 with e_add = 0, or c2 with e_add = eq - 47.
+  constexpr bool kFoldEq = D == 64 && (PACKED || QB == 1);
+  double c2q[QB];
   // The wave's query statistics for the exactness check of each key tile:
   // the largest 2^e_q and the largest L1 norm sum_c |q_c| over its rows.
   float wave_b = 0.0f, wave_a = 0.0f;
@@ -581,6 +595,7 @@ void attn_fwd_f32_kernel(
     mx = max_xor32(max_xor16_f32(mx));
     l1 = add_xor32(add_xor16_f32(l1));
     eq[qb] = row_exponent(mx);
+    c2q[qb] = kFoldEq ? __builtin_amdgcn_ldexp(c2, eq[qb] - 47) : c2;
     if (mx > 0.0f) wave_b = fmaxf(wave_b, __builtin_amdgcn_ldexpf(1.0f, eq[qb]));
     wave_a = fmaxf(wave_a, l1);
 #pragma unroll
@@ -813,7 +828,7 @@ void attn_fwd_f32_kernel(
               ks[h][a2] = __builtin_bit_cast(i32x4, lds_load16(kt, a2 * T::KSPLANEB + (kb * 16 + i16) * T::KSROW +
                                                                        (((4 * h + g) ^ kswz<D>(i16)) << 4)));
           const i32x4 ek = __builtin_bit_cast(i32x4, lds_load16(kt, T::KEXPB + (kb * 16 + 4 * g) * 4));
-          s[qb][kb] = score_block_f32<T>(ks, qs[qb], ek, eq[qb]);
+          s[qb][kb] = score_block_f32<T>(ks, qs[qb], ek, kFoldEq ? 0 : eq[qb] - 47);
         }
         if (!steady && key0 + KT > N) {
 #pragma unroll
@@ -822,7 +837,7 @@ void attn_fwd_f32_kernel(
             for (int r = 0; r < 4; ++r)
               if (key0 + kb * 16 + 4 * g + r >= N) s[qb][kb][r] = -INFINITY;
         }
-        softmax_block_f32<T>(s[qb], p[qb], m2[qb], l_run[qb], acc[qb], c2);
+        softmax_block_f32<T>(s[qb], p[qb], m2[qb], l_run[qb], acc[qb], c2q[qb]);
         // The next block reads the K slices from LDS again: without this the
         // compiler keeps every 16-key block's slices in registers from the
         // first block to the second, and the tile spills.
@@ -840,7 +855,7 @@ void attn_fwd_f32_kernel(
                 i32x4, lds_load16(kt, a2 * T::KSPLANEB + (kb * 16 + i16) * T::KSROW + (((4 * h + g) ^ kswz<D>(i16)) << 4)));
         const i32x4 ek = __builtin_bit_cast(i32x4, lds_load16(kt, T::KEXPB + (kb * 16 + 4 * g) * 4));
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = score_block_f32<T>(ks, qs[qb], ek, eq[qb]);
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = score_block_f32<T>(ks, qs[qb], ek, kFoldEq ? 0 : eq[qb] - 47);
       }
       if (!steady && key0 + KT > N) {
 #pragma unroll
@@ -854,7 +869,7 @@ void attn_fwd_f32_kernel(
           }
       }
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) softmax_block_f32<T>(s[qb], p[qb], m2[qb], l_run[qb], acc[qb], c2);
+      for (int qb = 0; qb < QB; ++qb) softmax_block_f32<T>(s[qb], p[qb], m2[qb], l_run[qb], acc[qb], c2q[qb]);
     }
 
     // ---- O^T += V^T P^T on the bf16 matrix cores, six piece products per
