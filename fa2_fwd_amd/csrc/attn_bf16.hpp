@@ -197,16 +197,23 @@ __global__ __launch_bounds__(T::NT) void attn_fwd_bf16_kernel(
   // ---- Q fragments (B operand of S^T = K Q^T): Q[row = i32][d = 16t + 8hh .. +7].
   // q_mode folds the sign of the scale into Q (+1 keep, -1 negate, 0 zero) so
   // that the softmax below always works with a positive log2-domain scale c2.
+  // Rows past the end load row N - 1 and are zeroed: every lane issues the
+  // same unconditional loads back to back (a load under a lane mask made the
+  // compiler wait for it on the spot, one HBM round trip before the K/V
+  // requests below).
   u32x4 qf[QB][D / 16];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qrow0 + qb * 32 + i32;
+    const __bf16* qrow = Qh + static_cast<size_t>(min(row, N - 1)) * D + 8 * hh;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) qf[qb][t] = *reinterpret_cast<const u32x4*>(qrow + 16 * t);
+    const bool zero = row >= N || q_mode == 0;
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < N) x = *reinterpret_cast<const u32x4*>(Qh + static_cast<size_t>(row) * D + 16 * t + 8 * hh);
+      u32x4 x = qf[qb][t];
       if (q_mode < 0) x ^= 0x80008000u;
-      if (q_mode == 0) x = u32x4{0u, 0u, 0u, 0u};
+      if (zero) x = u32x4{0u, 0u, 0u, 0u};
       qf[qb][t] = x;
     }
   }
