@@ -562,6 +562,70 @@ void attn_fwd_f32_kernel(
   float* Oh = O + head;
   const int qrow0 = qt * T::BR + wave * T::WQ;
 
+  const int ntiles = (N + KT - 1) / KT;
+  // Packed tiles: buffer b holds a tile's K part at smem + b * KPADB and its V
+  // part at smem + 2 KPADB + b * VPADB; each of the NT threads copies 16 bytes
+  // per round, wave w's lanes filling 1 KiB of the round.
+  const char* blobs = PACKED ? packed + static_cast<size_t>(bh) * static_cast<size_t>(ntiles) * T::PACKB : nullptr;
+  // The round moves the scalar source and LDS bases; the lane's offset is one
+  // register, recomputed from an opaque thread index (not kept across the loop).
+  // The LDS addresses are scalar: the buffer base plus this wave's 1 KiB.
+  const uint32_t wave_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)smem)) +
+                            1024u * static_cast<uint32_t>(uniform_sgpr(tid >> 6));
+  auto copy_tile = [&](int jj, int b) __attribute__((always_inline)) {
+    const char* src = blobs + static_cast<size_t>(jj) * T::PACKB;
+    const uint32_t kdst = wave_lds + b * T::KPADB;
+    const uint32_t vdst = wave_lds + 2 * T::KPADB + b * T::VPADB;
+    int voff = tid;
+    asm volatile("" : "+v"(voff));
+    voff *= 16;
+#pragma unroll
+    for (int u = 0; u < T::PCOPIES; ++u)
+      dma16_to(src + u * T::ROUNDB, voff,
+               u < T::KCOPIES ? kdst + u * T::ROUNDB : vdst + (u - T::KCOPIES) * T::ROUNDB);
+  };
+  // V item it of this thread: 32-key chunk c, key class g8 (keys
+  // 16 (i / 4) + 4 g8 + i % 4 of the chunk, i < 8) and column vcol.  Lanes of a
+  // wave take consecutive columns, so each of the 8 loads reads whole rows.
+  u32x4 kreg[T::LOADS];
+  float vreg[T::VITEMS][8];
+  // full: tile j lies wholly below N (no key needs the bounds check).
+  auto stage_load = [&](int j, auto full_tag) __attribute__((always_inline)) {
+    constexpr bool full = decltype(full_tag)::value;
+    // In the 256-row tile, an opaque copy of the thread index, as in
+    // stage_store: the per-lane address parts are recomputed here instead of
+    // being spilled across the key loop (and reloaded inside it).  The other
+    // tilings have the registers to keep them.
+    int tid_here = tid;
+    if constexpr (T::QB >= 2) asm volatile("" : "+v"(tid_here));
+#pragma unroll
+    for (int u = 0; u < T::LOADS; ++u) {
+      const int idx = tid_here + u * T::NT;
+      const int row = stage_row<D>(idx / T::CH), ch = idx % T::CH;
+      const int key = j * KT + row;
+      u32x4 kx = {0u, 0u, 0u, 0u};
+      if (full || key < N) kx = *reinterpret_cast<const u32x4*>(Kh + (key * D + ch * 4));
+      kreg[u] = kx;
+    }
+#pragma unroll
+    for (int it = 0; it < T::VITEMS; ++it) {
+      const int item = tid_here + it * T::NT;
+      const int vcol = item % D, cg = item / D;
+      const int c = cg >> 2, g8 = cg & 3;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int key = j * KT + 32 * c + 16 * (i >> 2) + 4 * g8 + (i & 3);
+        vreg[it][i] = (full || key < N) ? Vh[key * D + vcol] : 0.0f;
+      }
+    }
+  };
+  // The first K/V tile is requested before the Q loads, so that the two HBM
+  // round trips overlap.
+  if constexpr (PACKED)
+    copy_tile(0, 0);
+  else
+    stage_load(0, std::false_type{});
+
   // ---- Q slices (B operand of S^T): lane (i16, g) holds, for each 64-column
   // block h, columns 64h + 16g .. 64h + 16g + 15 of its query row, as five
   // int8 slices under the row's exponent eq.  q_mode folds the sign of the
@@ -576,18 +640,29 @@ void attn_fwd_f32_kernel(
   // The wave's query statistics for the exactness check of each key tile:
   // the largest 2^e_q and the largest L1 norm sum_c |q_c| over its rows.
   float wave_b = 0.0f, wave_a = 0.0f;
+  // Every query block's loads first, unconditional (rows past the end read
+  // row N - 1 and are zeroed below): a load under a lane mask is waited for
+  // on the spot.
+  f32x4 xq[QB][D / 64][4];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int h = 0; h < D / 64; ++h)
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+        xq[qb][h][t4] = *reinterpret_cast<const f32x4*>(
+            Qh + (min(qrow0 + qb * 16 + i16, N - 1) * D + 64 * h + 16 * g + 4 * t4));
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qrow0 + qb * 16 + i16;
     f32x4 x[D / 64][4];
     float mx = 0.0f, l1 = 0.0f;
+    const float qrow_mul = row < N ? qmul : 0.0f;
 #pragma unroll
     for (int h = 0; h < D / 64; ++h)
 #pragma unroll
       for (int t4 = 0; t4 < 4; ++t4) {
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (row < N) v = *reinterpret_cast<const f32x4*>(Qh + (row * D + 64 * h + 16 * g + 4 * t4));
-        v *= qmul;
+        const f32x4 v = xq[qb][h][t4] * qrow_mul;
         x[h][t4] = v;
         mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
         l1 += (fabsf(v[0]) + fabsf(v[1])) + (fabsf(v[2]) + fabsf(v[3]));
@@ -629,41 +704,6 @@ void attn_fwd_f32_kernel(
     for (int n = 0; n < D / 16; ++n) acc[qb][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  // V item it of this thread: 32-key chunk c, key class g8 (keys
-  // 16 (i / 4) + 4 g8 + i % 4 of the chunk, i < 8) and column vcol.  Lanes of a
-  // wave take consecutive columns, so each of the 8 loads reads whole rows.
-  u32x4 kreg[T::LOADS];
-  float vreg[T::VITEMS][8];
-  // full: tile j lies wholly below N (no key needs the bounds check).
-  auto stage_load = [&](int j, auto full_tag) __attribute__((always_inline)) {
-    constexpr bool full = decltype(full_tag)::value;
-    // In the 256-row tile, an opaque copy of the thread index, as in
-    // stage_store: the per-lane address parts are recomputed here instead of
-    // being spilled across the key loop (and reloaded inside it).  The other
-    // tilings have the registers to keep them.
-    int tid_here = tid;
-    if constexpr (T::QB >= 2) asm volatile("" : "+v"(tid_here));
-#pragma unroll
-    for (int u = 0; u < T::LOADS; ++u) {
-      const int idx = tid_here + u * T::NT;
-      const int row = stage_row<D>(idx / T::CH), ch = idx % T::CH;
-      const int key = j * KT + row;
-      u32x4 kx = {0u, 0u, 0u, 0u};
-      if (full || key < N) kx = *reinterpret_cast<const u32x4*>(Kh + (key * D + ch * 4));
-      kreg[u] = kx;
-    }
-#pragma unroll
-    for (int it = 0; it < T::VITEMS; ++it) {
-      const int item = tid_here + it * T::NT;
-      const int vcol = item % D, cg = item / D;
-      const int c = cg >> 2, g8 = cg & 3;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int key = j * KT + 32 * c + 16 * (i >> 2) + 4 * g8 + (i & 3);
-        vreg[it][i] = (full || key < N) ? Vh[key * D + vcol] : 0.0f;
-      }
-    }
-  };
   auto stage_store = [&](int buf) __attribute__((always_inline)) {
     char* kt = smem + buf * (T::KTILEB + T::VTILEB);
     char* vt = kt + T::KTILEB;
@@ -728,35 +768,12 @@ void attn_fwd_f32_kernel(
     }
   };
 
-  const int ntiles = (N + KT - 1) / KT;
-  // Packed tiles: buffer b holds a tile's K part at smem + b * KPADB and its V
-  // part at smem + 2 KPADB + b * VPADB; each of the NT threads copies 16 bytes
-  // per round, wave w's lanes filling 1 KiB of the round.
-  const char* blobs = PACKED ? packed + static_cast<size_t>(bh) * static_cast<size_t>(ntiles) * T::PACKB : nullptr;
-  // The round moves the scalar source and LDS bases; the lane's offset is one
-  // register, recomputed from an opaque thread index (not kept across the loop).
-  // The LDS addresses are scalar: the buffer base plus this wave's 1 KiB.
-  const uint32_t wave_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)smem)) +
-                            1024u * static_cast<uint32_t>(uniform_sgpr(tid >> 6));
-  auto copy_tile = [&](int jj, int b) __attribute__((always_inline)) {
-    const char* src = blobs + static_cast<size_t>(jj) * T::PACKB;
-    const uint32_t kdst = wave_lds + b * T::KPADB;
-    const uint32_t vdst = wave_lds + 2 * T::KPADB + b * T::VPADB;
-    int voff = tid;
-    asm volatile("" : "+v"(voff));
-    voff *= 16;
-#pragma unroll
-    for (int u = 0; u < T::PCOPIES; ++u)
-      dma16_to(src + u * T::ROUNDB, voff,
-               u < T::KCOPIES ? kdst + u * T::ROUNDB : vdst + (u - T::KCOPIES) * T::ROUNDB);
-  };
   if constexpr (PACKED) {
-    copy_tile(0, 0);
+    // tile 0 was requested before the Q loads
     vmcnt_wait<0>();
     __syncthreads();
   } else {
-    stage_load(0, std::false_type{});
-    stage_store(0);
+    stage_store(0);  // tile 0 was requested before the Q loads
     if (late && ntiles > 1) stage_load(1, std::false_type{});
     __syncthreads();
   }
