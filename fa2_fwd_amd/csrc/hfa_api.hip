@@ -80,10 +80,22 @@ constexpr int64_t kComputeUnits = 256;  // gfx950 (MI350 series): 8 XCDs x 32 CU
 bool fills_cus(int64_t BH, int64_t N, int64_t br) { return BH * ((N + br - 1) / br) >= kComputeUnits; }
 
 // fp32, d = 64 tiling of a shape: 2 = 256 rows, 1 = 128 rows, 0 = 64 rows.
+// Each tiling runs one workgroup per compute unit, so a launch takes
+// ceil(workgroups / CUs) rounds of one workgroup's time, which grows with its
+// rows over the tiling's throughput per row.  Relative throughputs measured
+// on the device (µs per row and key over many shapes): 128-row tiles 0.86
+// and 64-row tiles 0.6 of the 256-row tile's.  The tiling with the least
+// rounds x rows / throughput wins, the larger one on a tie.
+double f32_tiling_cost(int64_t BH, int64_t N, int64_t br, double rel_rate) {
+  const int64_t groups = BH * ((N + br - 1) / br);
+  return static_cast<double>((groups + kComputeUnits - 1) / kComputeUnits) * static_cast<double>(br) / rel_rate;
+}
 int f32_d64_tiling(int64_t BH, int64_t N) {
-  if (fills_cus(BH, N, F32D64Big::BR)) return 2;
-  if (fills_cus(BH, N, F32D64Small::BR)) return 1;
-  return 0;
+  const double big = f32_tiling_cost(BH, N, F32D64Big::BR, 1.0);
+  const double small = f32_tiling_cost(BH, N, F32D64Small::BR, 0.86);
+  const double tiny = f32_tiling_cost(BH, N, F32D64Tiny::BR, 0.6);
+  if (big <= small && big <= tiny) return 2;
+  return small <= tiny ? 1 : 0;
 }
 
 // Raise the dynamic-LDS limit of a kernel once per process (per device the

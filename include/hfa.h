@@ -110,9 +110,11 @@ hfa_status hfa_attn_fwd(const void* q, const void* k, const void* v, void* o, fl
 const char* hfa_status_str(hfa_status s);
 
 /* Query rows owned by one workgroup of the kernel hfa_attn_fwd selects for
- * this shape, i.e. the row-tile height B_r of its tiling (the fp32, d = 64
- * path uses 256 rows when B*H*ceil(N/256) workgroups still cover the 256
- * compute units of a gfx950, 128 otherwise); 0 for an unsupported dtype or
+ * this shape, i.e. the row-tile height B_r of its tiling (bf16: 256 rows;
+ * fp32, d = 64: 256, 128 or 64 rows, whichever needs the fewest rounds of
+ * workgroups over the 256 compute units of a gfx950 weighted by its measured
+ * time per row; fp32, d = 128: 128 rows when B*H*ceil(N/128) workgroups cover
+ * the compute units, else 64); 0 for an unsupported dtype or
  * head dim or a shape with B, H or N below 1.  Needs no device and makes no
  * HIP call. */
 int64_t hfa_block_rows(hfa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t d);

@@ -76,16 +76,25 @@ def test_block_rows_table():
 
 
 def test_block_rows_follow_the_shape():
-    # fp32 d=64 takes the largest workgroup whose grid still covers 256 CUs:
-    # 256 rows when B*H*ceil(N/256) >= 256 (the N=2048, B*H=32 workload), else
-    # 128 rows when B*H*ceil(N/128) >= 256 (the N=1024 workload), else 64.
-    assert hfa.hfa_block_rows(hfa.HFA_F32, 4, 8, 2048, 64) == 256
-    assert hfa.hfa_block_rows(hfa.HFA_F32, 4, 8, 1024, 64) == 128
+    # fp32 d=64 takes the tiling with the least rounds of workgroups (one per
+    # CU, 256 CUs) times rows per workgroup over its relative throughput per
+    # row (256 rows 1, 128 rows 0.86, 64 rows 0.6).
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 4, 8, 2048, 64) == 256  # one round of 256-row tiles
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 4, 8, 1024, 64) == 128  # one round of 128-row tiles
     assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 1, 128, 64) == 64
     assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 256, 200, 64) == 256
-    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 255, 256, 64) == 128
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 255, 256, 64) == 256
     assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 16, 1024, 64) == 64
     assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 8, 4096, 64) == 128
+    # 384 workgroups of 256 rows (two rounds, the second half empty) against
+    # 768 of 128 rows (three rounds): 128 rows
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 48, 2048, 64) == 128
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 80, 1024, 64) == 128
+    # 192 workgroups of 256 rows (one round) against 384 of 128 (two): 256 rows
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 48, 1024, 64) == 256
+    # one key tile or less: the shortest tile that still has the same rounds
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 256, 64, 64) == 64
+    assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 256, 128, 64) == 128
     # fp32 d=128 has two tilings: 128 rows when B*H*ceil(N/128) >= 256, else 64.
     assert hfa.hfa_block_rows(hfa.HFA_F32, 2, 8, 2048, 128) == 128
     assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 16, 2048, 128) == 128

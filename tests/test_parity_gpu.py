@@ -180,23 +180,26 @@ def test_f32_outlier_rows_in_one_tile():
 
 @pytest.mark.parametrize("N", [1, 64, 65, 128, 129, 192, 257, 320, 333, 449])
 def test_f32_d64_few_key_tiles(N):
-    # 256 heads put every N here on the 256-row tiling (one workgroup per CU at
-    # least), with 1 to 8 key tiles of 64: the waves that stage the next tile
-    # early request one tile further ahead, so the first tiles, the ragged
-    # last one and the switch from steady two-tile trips to single steps are
-    # all exercised.
+    # 256 heads with 1 to 8 key tiles of 64: the first tiles, the ragged last
+    # one and the switch from steady two-tile trips to single steps.  The
+    # library's tiling: 64-row tiles up to N = 64, 128-row ones up to 128 and
+    # where 256-row ones would take a second, mostly empty round (N = 257 to
+    # 384), else 256-row ones (N = 129 to 256 in one round, N = 449 in two
+    # rounds against four).
     B, H = 1, 256
-    assert hfa.hfa_block_rows(hfa.HFA_F32, B, H, N, 64) == 256
+    br = hfa.hfa_block_rows(hfa.HFA_F32, B, H, N, 64)
+    assert br == (64 if N <= 64 else 128 if N <= 128 or 256 < N <= 384 else 256)
     q, k, v = W.make_inputs(B, H, N, 64, "f32", seed=5000 + N, qk_mult=2.0)
     rows = W.sample_rows(N, 6, seed=N + 1)
-    check_case(f"f32 d=64 B=1 H=256 N={N} (few key tiles)", q, k, v, 0.125, "f32", rows=rows)
+    check_case(f"f32 d=64 B=1 H=256 N={N} (few key tiles, B_r={br})", q, k, v, 0.125, "f32", rows=rows)
 
 
 @pytest.mark.parametrize("B,H,N", [(1, 256, 200), (2, 64, 300), (1, 255, 256), (1, 4, 777), (1, 8, 4000),
                                    (1, 16, 1000), (1, 1, 65)])
 def test_f32_d64_all_tilings(B, H, N):
-    # fp32 d=64 takes 256-row workgroups when B*H*ceil(N/256) >= 256, 128-row
-    # ones when B*H*ceil(N/128) >= 256, else 64-row ones; all three, ragged N.
+    # fp32 d=64 chooses among 256-, 128- and 64-row workgroups by shape (the
+    # least rounds of workgroups times rows over the tiling's throughput): all
+    # three here (256: the first three, 128: H=8 N=4000, 64: the rest), ragged N.
     br = hfa.hfa_block_rows(hfa.HFA_F32, B, H, N, 64)
     q, k, v = W.make_inputs(B, H, N, 64, "f32", seed=B * 1000 + H + N, qk_mult=2.0)
     rows = W.sample_rows(N, 24, seed=N)
