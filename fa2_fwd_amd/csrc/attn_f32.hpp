@@ -520,13 +520,14 @@ __global__ __launch_bounds__(T::NT) void f32_pack_kernel(const float* __restrict
 // PACKED: K and V tiles come pre-formatted from f32_pack_kernel (`packed`,
 // [B*H][ntiles][PACKB]) and are copied into LDS as they are, with no staging
 // arithmetic; otherwise the workgroup formats every tile itself.
-template <class T, bool PACKED = false>
+//
 // 4-wave workgroups are compiled for two waves per SIMD, i.e. at most 256
 // registers a wave: allowed the whole register file, the compiler parks plain
 // values in accumulation registers and pays a v_accvgpr move for each use.
 #ifndef HFA_F32_NW4_WAVES_PER_EU
 #define HFA_F32_NW4_WAVES_PER_EU 2
 #endif
+template <class T, bool PACKED = false>
 __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(T::NW == 4 ? HFA_F32_NW4_WAVES_PER_EU : 1)))
 void attn_fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
