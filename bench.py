@@ -59,7 +59,7 @@ def log(msg: str) -> None:
 
 # The sources each operation's kernels and launch code are built from.
 OP_SOURCES = {
-    "attn": ("common.hpp", "api_util.hpp", "attn_bf16.hpp", "attn_f32.hpp", "hfa_api.hip"),
+    "attn": ("common.hpp", "api_util.hpp", "attn_bf16.hpp", "attn_bf16_solo.hpp", "attn_f32.hpp", "hfa_api.hip"),
     "softmax": ("common.hpp", "hbm_io.hpp", "api_util.hpp", "softmax_rows.hpp", "softmax_api.hip"),
     "rmsnorm": ("common.hpp", "hbm_io.hpp", "api_util.hpp", "rmsnorm.hpp", "rmsnorm_api.hip"),
 }

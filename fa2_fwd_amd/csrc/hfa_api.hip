@@ -11,6 +11,7 @@
 
 #include "hfa.h"
 #include "attn_bf16.hpp"
+#include "attn_bf16_solo.hpp"
 #include "attn_f32.hpp"
 #include "api_util.hpp"
 
@@ -64,6 +65,13 @@ using Bf16D128 = Bf16Tile<128, HFA_BF16_D128_TILE>;
 using Bf16D64 = Bf16Tile<64, HFA_BF16_D64_TILE>;
 using Bf16D64Long = Bf16Tile<64, HFA_BF16_D64_LONG_TILE>;
 constexpr int64_t kBf16LongKeys = 4096;
+// bf16, 128-row workgroups of 4 waves (no ping-pong) for grids of 256-row
+// workgroups that leave compute units idle and are not split.
+#ifndef HFA_BF16_SOLO
+#define HFA_BF16_SOLO 1
+#endif
+using Bf16SoloD128 = Bf16SoloTile<128>;
+using Bf16SoloD64 = Bf16SoloTile<64>;
 static_assert(Bf16D64Long::BR == Bf16D64::BR, "both d = 64 tilings cover the same query rows");
 using F32D64Big = F32Tile<64, HFA_F32_D64_BIG_TILE>;
 using F32D64Small = F32Tile<64, HFA_F32_D64_SMALL_TILE>;
@@ -211,6 +219,36 @@ hfa_status launch_bf16(const void* q, const void* k, const void* v, void* o, flo
   return HFA_OK;
 }
 
+template <class T>
+hfa_status launch_bf16_solo(const void* q, const void* k, const void* v, void* o, float* lse, int64_t BH,
+                            int64_t N, float scale, hipStream_t stream, bool launch) {
+  static std::once_flag flag;
+  static hipError_t err = hipSuccess;
+  auto kernel = attn_fwd_bf16_solo_kernel<T>;
+  if (ensure_lds(kernel, T::LDS_BYTES, flag, err) != HFA_OK) return HFA_ERR_LAUNCH;
+  if (!launch) return HFA_OK;
+  const int64_t n_qt = (N + T::BR - 1) / T::BR;
+  const int64_t total = BH * n_qt;
+  if (total > INT_MAX || BH * N > INT_MAX) return HFA_ERR_SHAPE;
+  const ScaleArgs sa = split_scale(scale);
+  hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(total)), dim3(T::NT), T::LDS_BYTES, stream,
+                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v),
+                     static_cast<__bf16*>(o), lse, static_cast<int>(N), static_cast<int>(n_qt),
+                     static_cast<int>(total), static_cast<float>(sa.c2), sa.q_mode);
+  return hipGetLastError() == hipSuccess ? HFA_OK : HFA_ERR_LAUNCH;
+}
+
+// Whether an unsplit bf16 call runs the 128-row 4-wave kernel: its grid
+// (twice the 256-row one) still fits one round over the compute units, and at
+// d = 128 the heads are short (N <= 1024).  Measured: the lone wave's key tile
+// costs about what the ping-pong pair's does (1.1 against 1.0 us at d = 128,
+// less at d = 64, where the pair is bound by its two vector phases), so the
+// doubled workgroups and the shorter prologue pay on few, short tiles only.
+bool bf16_solo(int64_t BH, int64_t N, int64_t d) {
+  const int64_t grid = BH * ((N + Bf16D128::BR - 1) / Bf16D128::BR);
+  return HFA_BF16_SOLO && 2 * grid <= kComputeUnits && (d == 64 || N <= 1024);
+}
+
 // Bytes of pre-formatted K/V tiles (f32_pack_kernel) for B*H heads of N keys.
 template <class T>
 int64_t f32_pack_bytes(int64_t BH, int64_t N) {
@@ -281,6 +319,10 @@ hfa_status dispatch(const void* q, const void* k, const void* v, void* o, float*
                     int64_t d, float scale, hfa_dtype dtype, hipStream_t st, bool launch, KeySplit ks = {1, 0},
                     void* work = nullptr) {
   if (dtype == HFA_BF16) {
+    if (ks.nsplit == 1 && bf16_solo(BH, N, d)) {
+      if (d == 128) return launch_bf16_solo<Bf16SoloD128>(q, k, v, o, lse, BH, N, scale, st, launch);
+      return launch_bf16_solo<Bf16SoloD64>(q, k, v, o, lse, BH, N, scale, st, launch);
+    }
     if (d == 128) return launch_bf16<Bf16D128>(q, k, v, o, lse, BH, N, scale, st, launch, ks, work);
     if (ks.nsplit == 1 && N >= kBf16LongKeys)
       return launch_bf16<Bf16D64Long, false>(q, k, v, o, lse, BH, N, scale, st, launch);
@@ -367,8 +409,10 @@ extern "C" {
 
 int64_t hfa_block_rows(hfa_dtype dtype, int64_t B, int64_t H, int64_t N, int64_t d) {
   if (B < 1 || H < 1 || N < 1 || B > INT64_MAX / H) return 0;
-  if (dtype == HFA_BF16 && d == 128) return Bf16D128::BR;
-  if (dtype == HFA_BF16 && d == 64) return Bf16D64::BR;
+  if (dtype == HFA_BF16 && (d == 64 || d == 128)) {
+    if (bf16_solo(B * H, N, d)) return Bf16SoloD128::BR;  // unsplit calls; a key split keeps 256 rows
+    return d == 128 ? Bf16D128::BR : Bf16D64::BR;
+  }
   if (dtype == HFA_F32 && d == 64) {
     const int t = f32_d64_tiling(B * H, N);
     return t == 2 ? F32D64Big::BR : t == 1 ? F32D64Small::BR : F32D64Tiny::BR;

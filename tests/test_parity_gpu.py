@@ -206,6 +206,18 @@ def test_f32_d64_all_tilings(B, H, N):
     check_case(f"f32 d=64 B={B} H={H} N={N} (B_r={br})", q, k, v, 0.125, "f32", rows=rows)
 
 
+@pytest.mark.parametrize("B,H,N,d", [(1, 16, 1024, 128), (1, 1, 1, 128), (1, 1, 65, 128), (1, 5, 1000, 128),
+                                     (2, 3, 333, 64), (4, 8, 1024, 64), (1, 2, 3000, 64), (1, 2, 1537, 64)])
+def test_bf16_small_grid_kernel(B, H, N, d):
+    # The 128-row 4-wave kernel (no ping-pong; every wave streams its quarter
+    # of both K and V through 3-deep rings): one key tile, a ragged first or
+    # last tile, many tiles, both head dims.
+    assert hfa.hfa_block_rows(hfa.HFA_BF16, B, H, N, d) == 128
+    q, k, v = W.make_inputs(B, H, N, d, "bf16", seed=B * 100 + H * 10 + N + d)
+    rows = None if N <= 1100 else W.sample_rows(N, 48, seed=N + d)
+    check_case(f"bf16 4-wave B={B} H={H} N={N} d={d}", q, k, v, 1.0 / math.sqrt(d), "bf16", rows=rows)
+
+
 @pytest.mark.parametrize("B,H,N", [(1, 4, 4096), (1, 16, 1024), (2, 2, 1500), (1, 1, 33), (2, 8, 2048),
                                    (1, 16, 2047)])
 def test_f32_d128_both_tilings(B, H, N):
