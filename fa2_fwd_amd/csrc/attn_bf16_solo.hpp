@@ -56,11 +56,16 @@ __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void
 
   const int tid = thread_id();
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = uniform_sgpr(tid >> 6);
   const int i32 = lane & 31, hh = lane >> 5;
 
+  // Workgroup-uniform indices in scalar registers, so that the request
+  // addresses below are formed with scalar arithmetic: a vector write of a
+  // scalar operand would need wait states before the inline-assembly load
+  // reads it, which the compiler does not insert.
   const int tile = xcd_remap(group_id(), total_wg);
-  const int bh = tile / n_qt, qt = tile - bh * n_qt;
+  const int bh = uniform_sgpr(tile / n_qt);
+  const int qt = uniform_sgpr(tile - bh * n_qt);
   const size_t head = static_cast<size_t>(bh) * static_cast<size_t>(N) * D;
   const __bf16* Qh = Q + head;
   const __bf16* Kh = K + head;
@@ -80,31 +85,34 @@ __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     koff[u] = (row * D + (phys ^ k_swz<T::CH>(row)) * 8) * 2;
     voff[u] = (row * D + (phys ^ v_swz<T::CH>(row)) * 8) * 2;
   }
+  // This wave's LDS destination within a tile buffer, as a scalar LDS address.
+  const uint32_t wave_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)smem)) +
+                            static_cast<uint32_t>(wave * T::LD * 1024);
   auto issue_tile = [&](int t) __attribute__((always_inline)) {
     if (t >= ntiles) return;
     const int slot = t % NBUF;
     const char* ksrc = reinterpret_cast<const char*>(Kh + static_cast<size_t>(t) * KT * D);
     const char* vsrc = reinterpret_cast<const char*>(Vh + static_cast<size_t>(t) * KT * D);
-    char* kdst = kbuf + slot * TILEB + wave * T::LD * 1024;
-    char* vdst = vbuf + slot * TILEB + wave * T::LD * 1024;
+    const uint32_t kdst = wave_lds + static_cast<uint32_t>(slot * TILEB);
+    const uint32_t vdst = wave_lds + static_cast<uint32_t>((NBUF + slot) * TILEB);
     if ((t + 1) * KT <= N) {
 #pragma unroll
-      for (int u = 0; u < T::LD; ++u) dma16(ksrc, koff[u], kdst + u * 1024);
+      for (int u = 0; u < T::LD; ++u) dma16_to(ksrc, koff[u], kdst + u * 1024);
 #pragma unroll
-      for (int u = 0; u < T::LD; ++u) dma16(vsrc, voff[u], vdst + u * 1024);
+      for (int u = 0; u < T::LD; ++u) dma16_to(vsrc, voff[u], vdst + u * 1024);
     } else {  // ragged last tile: rows past the end re-read the last row
       const int last = N - 1 - t * KT;
 #pragma unroll
       for (int u = 0; u < T::LD; ++u) {
         const int row = ((wave * T::LD + u) * 64 + lane) / T::CH;
         const int back = row > last ? (row - last) * D * 2 : 0;
-        dma16(ksrc, koff[u] - back, kdst + u * 1024);
+        dma16_to(ksrc, koff[u] - back, kdst + u * 1024);
       }
 #pragma unroll
       for (int u = 0; u < T::LD; ++u) {
         const int row = ((wave * T::LD + u) * 64 + lane) / T::CH;
         const int back = row > last ? (row - last) * D * 2 : 0;
-        dma16(vsrc, voff[u] - back, vdst + u * 1024);
+        dma16_to(vsrc, voff[u] - back, vdst + u * 1024);
       }
     }
   };
