@@ -107,3 +107,47 @@ def test_wait_counts_within_spelled_out_cases(ring):
             for newest, need in checks:
                 after = min(newest, ntiles - 1) - need
                 assert after <= min(AHEAD - 1, 3)
+
+
+# ---- the 128-row 4-wave kernel (attn_bf16_solo.hpp): one interval per key
+# tile.  Step j: each wave waits for its own requests of tile j (at most the
+# requests of tile j + 1 may stay in flight), barrier, then requests tile
+# j + AHEAD into slot (j + AHEAD) % NBUF, reads tile j (K for the scores, V
+# for the output products).  The model mirrors that kernel's loop.
+SOLO_NBUF, SOLO_AHEAD = 3, 2
+
+
+def solo_events(ntiles):
+    requested = {}  # tile -> step in which it is requested (-1: prologue)
+    for t in range(min(SOLO_AHEAD, ntiles)):
+        requested[t] = -1
+    reads, waits = [], {}
+    for j in range(ntiles):
+        in_flight_after = [t for t in requested if t > j]
+        waits[j] = len(in_flight_after)  # tiles whose requests may stay outstanding
+        if j + SOLO_AHEAD < ntiles:
+            requested[j + SOLO_AHEAD] = j
+        reads.append((j, j))  # (step, tile)
+    return requested, reads, waits
+
+
+@pytest.mark.parametrize("ntiles", range(1, 12))
+def test_solo_ring(ntiles):
+    requested, reads, waits = solo_events(ntiles)
+    assert sorted(requested) == list(range(ntiles))
+    for step, tile in reads:
+        # requested before this step's barrier, and complete by its wait: the
+        # kernel lets exactly one newer tile stay in flight (none on the last)
+        assert requested[tile] < step or requested[tile] == -1
+        assert waits[step] == (0 if step == ntiles - 1 else 1)
+    for t, step in requested.items():
+        if step < 0:
+            continue
+        slot = t % SOLO_NBUF
+        # the refill of a slot comes after the barrier of the step that follows
+        # the last read of its previous tile (t - NBUF), and never in a step that
+        # reads the same slot
+        prev = t - SOLO_NBUF
+        if prev >= 0:
+            assert step > prev
+        assert all(r_tile % SOLO_NBUF != slot for r_step, r_tile in reads if r_step == step)
