@@ -11,10 +11,14 @@
 // O^T = V^T P^T), the LDS swizzles, the log2-domain lazy running max and the
 // epilogue.  What differs is the streaming: every wave requests its quarter
 // of both the K and the V tile (global_load_lds_dwordx4, HBM straight to
-// LDS) into rings of NBUF = 3 tiles, AHEAD = 2 tiles ahead, and one barrier
-// per tile separates the tiles: after it, tile j is complete in LDS (each
-// wave waited for its own requests first) and no wave still reads tile j - 1,
-// whose slot then takes tile j + 2.
+// LDS), AHEAD = 2 tiles ahead, and one barrier per step separates the steps.
+// Step j computes the scores of tile j, then the output products of tile
+// j - 1 (which keep the matrix core busy during the softmax of tile j, the
+// order of the 256-row kernel's MFMA phase), then that softmax.  So K_j is
+// read in step j and V_j in step j + 1: K has a ring of 3 tiles, V one of 4.
+// After the barrier of step j, tile j is complete in LDS (each wave waited
+// for its own requests first) and no wave still reads K_{j-1} or V_{j-2},
+// whose slots then take tile j + 2.
 #pragma once
 
 #include "attn_bf16.hpp"
@@ -32,10 +36,11 @@ struct Bf16SoloTile {
   static constexpr int ROWB = D * 2;  // bytes per K or V row in LDS (XOR-swizzled, unpadded)
   static constexpr int TILEB = KT * ROWB;
   static constexpr int CH = D / 8;   // 16-byte chunks per row
-  static constexpr int NBUF = 3;     // LDS ring depth, tiles per tensor
+  static constexpr int NBUF = 3;     // K ring depth (tiles)
+  static constexpr int NBUF_V = 4;   // V ring depth: V_j is read one step after K_j
   static constexpr int AHEAD = NBUF - 1;
   static constexpr int LD = TILEB / (NW * 64 * 16);  // 16-byte requests per lane per tile and tensor
-  static constexpr int LDS_BYTES = 2 * NBUF * TILEB;  // K ring and V ring
+  static constexpr int LDS_BYTES = (NBUF + NBUF_V) * TILEB;  // K ring, then V ring
   static_assert(LD >= 1 && TILEB % (NW * 64 * 16) == 0, "a tile must split into whole load instructions");
   static_assert(CH == 8 || CH == 16, "swizzles are defined for d = 64 and d = 128");
   static_assert(KT % 32 == 0, "whole 32-key MFMA blocks");
@@ -94,7 +99,7 @@ __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     const char* ksrc = reinterpret_cast<const char*>(Kh + static_cast<size_t>(t) * KT * D);
     const char* vsrc = reinterpret_cast<const char*>(Vh + static_cast<size_t>(t) * KT * D);
     const uint32_t kdst = wave_lds + static_cast<uint32_t>(slot * TILEB);
-    const uint32_t vdst = wave_lds + static_cast<uint32_t>((NBUF + slot) * TILEB);
+    const uint32_t vdst = wave_lds + static_cast<uint32_t>((NBUF + t % T::NBUF_V) * TILEB);
     if ((t + 1) * KT <= N) {
 #pragma unroll
       for (int u = 0; u < T::LD; ++u) dma16_to(ksrc, koff[u], kdst + u * 1024);
@@ -160,6 +165,22 @@ __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[n][r] = 0.0f;
   float m2 = -INFINITY, l_run = 0.0f;  // running max (log2 units) and denominator
+  bf16x8 pf[KT / 16];                  // P of the last softmax, consumed one step later
+
+  // ---- O^T += V_t^T P_t^T: key chunk c of 16 keys, column block n of 32
+  auto output_products = [&](int t) __attribute__((always_inline)) {
+    const char* vt = vbuf + (t % T::NBUF_V) * TILEB;
+#pragma unroll
+    for (int c = 0; c < KT / 16; ++c)
+#pragma unroll
+      for (int n = 0; n < D / 32; ++n) {
+        const int off = vlane[n] + 16 * c * ROWB;
+        const s16x4 lo = lds_read_tr16(vt, off);
+        const s16x4 hi = lds_read_tr16(vt, off + 4 * ROWB);
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], acc[n], 0, 0, 0);
+      }
+  };
 
   // One key tile.  first: tile 0 (the running max starts at its row max);
   // last: the final tile (nothing requested after it; keys past N masked).
@@ -174,9 +195,8 @@ __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     else
       vmcnt_wait<2 * T::LD>();
     lds_barrier();
-    issue_tile(j + T::AHEAD);  // into the slot of tile j - 1
+    issue_tile(j + T::AHEAD);  // K into the slot of K_{j-1}, V into that of V_{j-2}
     const char* kt = kbuf + (j % NBUF) * TILEB;
-    const char* vt = vbuf + (j % NBUF) * TILEB;
 
     // ---- S^T = K_j Q^T: lane (i32, hh) register r of s[kb] holds key
     // 32 kb + 16 (r / 8) + 8 hh + r % 8 of the tile for query i32.
@@ -204,6 +224,11 @@ __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void
           if (key0 + kb * 32 + 16 * (r >> 3) + 8 * hh + (r & 7) >= N) s[kb][r] = -INFINITY;
     }
 
+    // ---- the previous tile's output products: independent of this tile's
+    // softmax, they keep the matrix core busy while it runs (the order of the
+    // 256-row kernel's MFMA phase: scores of tile j, then P_{j-1} V_{j-1})
+    if constexpr (!first) output_products(j - 1);
+
     // ---- online softmax (log2 domain, lazy running max: see attn_bf16.hpp)
     constexpr int NS = KT / 2;
     auto xv = [&](int i) { return s[i / 16][i % 16]; };
@@ -219,7 +244,6 @@ __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void
         for (int u = 0; u < w; ++u) part[u] = fmaxf(part[u], part[u + w]);
       return max_xor32(part[0]);
     };
-    bf16x8 pf[KT / 16];
     auto weights = [&]() {
       float pv[NS];
 #pragma unroll
@@ -267,18 +291,6 @@ __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void
       }
     }
     l_run += tsum;
-
-    // ---- O^T += V_j^T P_j^T: key chunk c of 16 keys, column block n of 32
-#pragma unroll
-    for (int c = 0; c < KT / 16; ++c)
-#pragma unroll
-      for (int n = 0; n < D / 32; ++n) {
-        const int off = vlane[n] + 16 * c * ROWB;
-        const s16x4 lo = lds_read_tr16(vt, off);
-        const s16x4 hi = lds_read_tr16(vt, off + 4 * ROWB);
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        acc[n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[c], acc[n], 0, 0, 0);
-      }
   };
   if (ntiles == 1) {
     step(0, std::true_type{}, std::true_type{});
@@ -287,6 +299,7 @@ __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     for (int j = 1; j + 1 < ntiles; ++j) step(j, std::false_type{}, std::false_type{});
     step(ntiles - 1, std::false_type{}, std::true_type{});
   }
+  output_products(ntiles - 1);  // tile ntiles - 1 is complete since the last step's wait
 
   // ---- epilogue: normalise, round to bf16, one write of O and of LSE
   const float l_tot = add_xor32(l_run);

@@ -70,6 +70,9 @@ constexpr int64_t kBf16LongKeys = 4096;
 #ifndef HFA_BF16_SOLO
 #define HFA_BF16_SOLO 1
 #endif
+#ifndef HFA_BF16_SOLO_MAX_N_D128
+#define HFA_BF16_SOLO_MAX_N_D128 4096
+#endif
 using Bf16SoloD128 = Bf16SoloTile<128>;
 using Bf16SoloD64 = Bf16SoloTile<64>;
 static_assert(Bf16D64Long::BR == Bf16D64::BR, "both d = 64 tilings cover the same query rows");
@@ -240,13 +243,13 @@ hfa_status launch_bf16_solo(const void* q, const void* k, const void* v, void* o
 
 // Whether an unsplit bf16 call runs the 128-row 4-wave kernel: its grid
 // (twice the 256-row one) still fits one round over the compute units, and at
-// d = 128 the heads are short (N <= 1024).  Measured: the lone wave's key tile
-// costs about what the ping-pong pair's does (1.1 against 1.0 us at d = 128,
-// less at d = 64, where the pair is bound by its two vector phases), so the
-// doubled workgroups and the shorter prologue pay on few, short tiles only.
+// d = 128 N <= 4096.  Measured against the 256-row kernel: 9-25 % faster on
+// such grids (N = 333 to 3000 at d = 64, 128 to 2048 at d = 128), +3 % at
+// d = 128, N = 4096, and 1.5 % slower at N = 8192, where the ping-pong pair's
+// overlap of two waves per SIMD outweighs the doubled workgroups.
 bool bf16_solo(int64_t BH, int64_t N, int64_t d) {
   const int64_t grid = BH * ((N + Bf16D128::BR - 1) / Bf16D128::BR);
-  return HFA_BF16_SOLO && 2 * grid <= kComputeUnits && (d == 64 || N <= 1024);
+  return HFA_BF16_SOLO && 2 * grid <= kComputeUnits && (d == 64 || N <= HFA_BF16_SOLO_MAX_N_D128);
 }
 
 // Bytes of pre-formatted K/V tiles (f32_pack_kernel) for B*H heads of N keys.

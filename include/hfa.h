@@ -112,7 +112,7 @@ const char* hfa_status_str(hfa_status s);
 /* Query rows owned by one workgroup of the kernel hfa_attn_fwd selects for
  * this shape, i.e. the row-tile height B_r of its tiling (bf16: 256 rows, or
  * 128 where at most 128 workgroups of 256 rows would run, at d = 64, and at
- * d = 128 with N <= 1024; a key split of hfa_attn_fwd_split keeps 256;
+ * d = 128 with N <= 4096; a key split of hfa_attn_fwd_split keeps 256;
  * fp32, d = 64: 256, 128 or 64 rows, whichever needs the fewest rounds of
  * workgroups over the 256 compute units of a gfx950 weighted by its measured
  * time per row; fp32, d = 128: 128 rows when B*H*ceil(N/128) workgroups cover

@@ -97,12 +97,14 @@ def test_block_rows_follow_the_shape():
     assert hfa.hfa_block_rows(hfa.HFA_F32, 1, 256, 128, 64) == 128
     # bf16: 256-row ping-pong workgroups, or 128-row 4-wave ones for unsplit
     # calls whose 256-row grid has at most 128 workgroups (at d=128 only for
-    # N <= 1024).
+    # N <= 4096).
     assert hfa.hfa_block_rows(hfa.HFA_BF16, 1, 16, 16384, 128) == 256
     assert hfa.hfa_block_rows(hfa.HFA_BF16, 2, 32, 4096, 128) == 256
     assert hfa.hfa_block_rows(hfa.HFA_BF16, 1, 16, 1024, 128) == 128
     assert hfa.hfa_block_rows(hfa.HFA_BF16, 1, 1, 128, 128) == 128
-    assert hfa.hfa_block_rows(hfa.HFA_BF16, 1, 16, 2048, 128) == 256
+    assert hfa.hfa_block_rows(hfa.HFA_BF16, 1, 16, 2048, 128) == 128
+    assert hfa.hfa_block_rows(hfa.HFA_BF16, 1, 1, 8192, 128) == 256
+    assert hfa.hfa_block_rows(hfa.HFA_BF16, 1, 32, 2048, 128) == 256
     assert hfa.hfa_block_rows(hfa.HFA_BF16, 4, 8, 1024, 64) == 128
     assert hfa.hfa_block_rows(hfa.HFA_BF16, 1, 4, 4096, 64) == 128
     assert hfa.hfa_block_rows(hfa.HFA_BF16, 2, 16, 1536, 64) == 256

@@ -207,7 +207,8 @@ def test_f32_d64_all_tilings(B, H, N):
 
 
 @pytest.mark.parametrize("B,H,N,d", [(1, 16, 1024, 128), (1, 1, 1, 128), (1, 1, 65, 128), (1, 5, 1000, 128),
-                                     (2, 3, 333, 64), (4, 8, 1024, 64), (1, 2, 3000, 64), (1, 2, 1537, 64)])
+                                     (2, 3, 333, 64), (4, 8, 1024, 64), (1, 2, 3000, 64), (1, 2, 1537, 64),
+                                     (1, 8, 2048, 128)])
 def test_bf16_small_grid_kernel(B, H, N, d):
     # The 128-row 4-wave kernel (no ping-pong; every wave streams its quarter
     # of both K and V through 3-deep rings): one key tile, a ragged first or

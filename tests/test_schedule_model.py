@@ -109,45 +109,48 @@ def test_wait_counts_within_spelled_out_cases(ring):
                 assert after <= min(AHEAD - 1, 3)
 
 
-# ---- the 128-row 4-wave kernel (attn_bf16_solo.hpp): one interval per key
-# tile.  Step j: each wave waits for its own requests of tile j (at most the
+# ---- the 128-row 4-wave kernel (attn_bf16_solo.hpp): one barrier per step.
+# Step j: each wave waits for its own requests of tile j (at most the
 # requests of tile j + 1 may stay in flight), barrier, then requests tile
-# j + AHEAD into slot (j + AHEAD) % NBUF, reads tile j (K for the scores, V
-# for the output products).  The model mirrors that kernel's loop.
-SOLO_NBUF, SOLO_AHEAD = 3, 2
+# j + AHEAD (K into slot (j + AHEAD) % NBUF_K, V into slot (j + AHEAD) %
+# NBUF_V), reads K_j for the scores and V_{j-1} for the output products of
+# the previous tile; V_{ntiles-1} is read after the last step.
+SOLO_NBUF_K, SOLO_NBUF_V, SOLO_AHEAD = 3, 4, 2
 
 
 def solo_events(ntiles):
-    requested = {}  # tile -> step in which it is requested (-1: prologue)
-    for t in range(min(SOLO_AHEAD, ntiles)):
-        requested[t] = -1
-    reads, waits = [], {}
+    requested = {t: -1 for t in range(min(SOLO_AHEAD, ntiles))}  # tile -> step (-1: prologue)
+    reads = []  # (step, tensor, tile); step ntiles = after the loop
+    in_flight = {}
     for j in range(ntiles):
-        in_flight_after = [t for t in requested if t > j]
-        waits[j] = len(in_flight_after)  # tiles whose requests may stay outstanding
+        in_flight[j] = len([t for t in requested if t > j])
         if j + SOLO_AHEAD < ntiles:
             requested[j + SOLO_AHEAD] = j
-        reads.append((j, j))  # (step, tile)
-    return requested, reads, waits
+        reads.append((j, "K", j))
+        if j > 0:
+            reads.append((j, "V", j - 1))
+    reads.append((ntiles, "V", ntiles - 1))
+    return requested, reads, in_flight
 
 
 @pytest.mark.parametrize("ntiles", range(1, 12))
 def test_solo_ring(ntiles):
-    requested, reads, waits = solo_events(ntiles)
+    requested, reads, in_flight = solo_events(ntiles)
     assert sorted(requested) == list(range(ntiles))
-    for step, tile in reads:
-        # requested before this step's barrier, and complete by its wait: the
-        # kernel lets exactly one newer tile stay in flight (none on the last)
-        assert requested[tile] < step or requested[tile] == -1
-        assert waits[step] == (0 if step == ntiles - 1 else 1)
+    for j in range(ntiles):
+        # the kernel lets exactly one newer tile stay in flight (none on the last step)
+        assert in_flight[j] == (0 if j == ntiles - 1 else 1)
+    for step, tensor, tile in reads:
+        # complete by the wait of step `tile`, whose barrier precedes the read
+        assert tile <= step and (requested[tile] < tile or requested[tile] == -1)
     for t, step in requested.items():
         if step < 0:
             continue
-        slot = t % SOLO_NBUF
-        # the refill of a slot comes after the barrier of the step that follows
-        # the last read of its previous tile (t - NBUF), and never in a step that
-        # reads the same slot
-        prev = t - SOLO_NBUF
-        if prev >= 0:
-            assert step > prev
-        assert all(r_tile % SOLO_NBUF != slot for r_step, r_tile in reads if r_step == step)
+        for tensor, depth in (("K", SOLO_NBUF_K), ("V", SOLO_NBUF_V)):
+            # the slot's previous tile is last read before this step's barrier,
+            # and no read in this step uses the slot being refilled
+            prev = t - depth
+            if prev >= 0:
+                assert all(r_step < step for r_step, r_tensor, r_tile in reads if r_tensor == tensor and r_tile == prev)
+            assert all(r_tile % depth != t % depth for r_step, r_tensor, r_tile in reads
+                       if r_step == step and r_tensor == tensor)
